@@ -1,0 +1,203 @@
+/*
+ * pa.h -- C ABI of libpa: the PagedAttention hot path on MI355X (gfx950).
+ *
+ * Pages cited (titles as published; sections as numbered on each page):
+ *   [P1] "12. 推理加速(二): nano-vllm — 1200 行手写 vLLM": §12.6 (Attention layer:
+ *        paged KV cache -- the store kernel and the two FlashAttention calls),
+ *        §12.7 (ModelRunner: KV-cache allocation, prepare_prefill/decode,
+ *        CUDA-graph padding).
+ *   [P2] kyonqi, "nano-vllm 05" (ModelRunner): prepare_prefill, prepare_decode,
+ *        prepare_block_tables, run_model.
+ *   [P4] "vLLM 深度解读", §3 (PagedAttention CUDA kernel sketch).
+ *   [P5] "Nano-vLLM 源码解读 - 3. PagedAttention": §3 (two-step mapping),
+ *        §4 (slot_mapping protocol; prefill and decode paths), §5 (block size).
+ *
+ * Common conventions
+ *   - bf16 tensors are passed as untyped pointers to IEEE bfloat16 data.
+ *   - A KV cache is ONE layer's pool, [num_blocks, block_size, num_kv_heads,
+ *     head_dim], contiguous (the per-layer view of the engine's pool, [P1
+ *     §12.7]). A "slot" is a row index into it viewed as
+ *     [num_blocks * block_size, num_kv_heads * head_dim].
+ *   - Pointers named as device pointers must point to device memory (or
+ *     memory the device can read); host pointers to host memory. The caller
+ *     owns every buffer. The library never allocates or frees memory; its only
+ *     global state is a per-thread error message.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Every
+ *     device entry point only enqueues work on it and returns; nothing
+ *     synchronises.
+ *   - Return value: PA_OK (0) or a negative PA_ERR_* code; pa_last_error()
+ *     then describes the problem. Host-side checks never read device memory;
+ *     device-resident preconditions (slots, table entries, lengths) are the
+ *     caller's to keep and are listed per function.
+ *   - Supported shapes: head_dim 64 or 128; block_size 256; num_q_heads a
+ *     multiple of num_kv_heads with group size G = num_q_heads / num_kv_heads
+ *     in {1, 2, 4, 8}. Others return PA_ERR_UNSUPPORTED.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_OK 0
+#define PA_ERR_INVALID_ARG (-1) /* null pointer, bad size/stride/alignment  */
+#define PA_ERR_UNSUPPORTED (-2) /* shape outside the compiled set           */
+#define PA_ERR_WORKSPACE (-3)   /* workspace missing or too small           */
+#define PA_ERR_HIP (-4)         /* the HIP runtime reported a launch error  */
+
+/* Geometry of one layer's cache. */
+typedef struct pa_desc {
+  int32_t num_q_heads;  /* H_q                                               */
+  int32_t num_kv_heads; /* H_kv; q-head h reads kv-head h / (H_q / H_kv)     */
+  int32_t head_dim;     /* d: 64 or 128                                      */
+  int32_t block_size;   /* B: tokens per physical block; 256 ([P5 §5])       */
+  int64_t num_blocks;   /* N: physical blocks in the pool                    */
+} pa_desc;
+
+/*
+ * pa_store_kv -- scatter new tokens' K and V into the paged cache.
+ * [P1 §12.6] store kernel; slot protocol [P5 §4].
+ *
+ * For every i < n_tokens with s = slot_mapping[i] != -1, copies the
+ * H_kv*d bf16 values of k[i] into k_cache row s and those of v[i] into
+ * v_cache row s, bit for bit. s == -1 is a padding entry and is skipped
+ * (the graph-replay padding of [P1 §12.7]). Rows not named are untouched.
+ *
+ *   k, v          device, bf16 [n_tokens, H_kv, d]; the last two dims are
+ *                 contiguous (head stride d) and token i starts at element
+ *                 i * k_row_stride (resp. v_row_stride). The strides let k/v
+ *                 be views of a fused qkv projection output.
+ *   k_row_stride, v_row_stride   elements, >= H_kv*d.
+ *   k_cache, v_cache  device, bf16 [N, B, H_kv, d], contiguous.
+ *   slot_mapping  device, int32 [n_tokens]; each entry -1 or in [0, N*B);
+ *                 entries other than -1 must be distinct (otherwise the
+ *                 surviving value is unspecified).
+ *   n_tokens      >= 0; 0 is a successful no-op.
+ * Alignment: any; a 16-byte path is used when pointers and strides allow.
+ */
+int pa_store_kv(const void* k, int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t n_tokens,
+                const pa_desc* desc, void* stream);
+
+/*
+ * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for
+ * this batch geometry (split-K partial results). Returns 0 on invalid
+ * arguments. The result depends only on the arguments.
+ */
+size_t pa_decode_workspace_size(const pa_desc* desc, int32_t num_seqs, int32_t max_context_len);
+
+/*
+ * pa_decode -- paged decode attention, one query per sequence.
+ * [P1 §12.6] decode branch (flash_attn_with_kvcache over the block table),
+ * [P4 §3] kernel sketch (block-table read, online softmax), GQA grouping.
+ *
+ * For each sequence b and q-head h, with g = h / (H_q / H_kv) and
+ * n = context_lens[b]:
+ *   out[b,h,:] = sum_t softmax_t(scale * q[b,h,:] . K_t) * V_t,   t < n,
+ * where K_t, V_t are the kv-head-g rows of token t, found at slot
+ * block_tables[b][t / B] * B + t % B ([P5 §3]). n includes the token just
+ * stored, so pa_store_kv runs first on the same stream. n == 0 marks a
+ * padding row: its output is all zeros and nothing is read for it.
+ * Accumulation is fp32; out is rounded to bf16 (nearest, ties to even).
+ *
+ *   q             device, bf16 [num_seqs, H_q, d], contiguous.
+ *   k_cache, v_cache  device, bf16 [N, B, H_kv, d].
+ *   block_tables  device, int32 [num_seqs, max_blocks_per_seq] row-major;
+ *                 entries for blocks 0 .. ceil(n/B)-1 must be in [0, N); the
+ *                 rest are padding (-1 by convention, [P2 prepare_block_tables])
+ *                 and are never read.
+ *   context_lens  device, int32 [num_seqs]; 0 <= n <= max_context_len and
+ *                 ceil(n/B) <= max_blocks_per_seq.
+ *   max_context_len  host upper bound of context_lens (sizes the grid).
+ *   scale         softmax scale, e.g. 1/sqrt(d).
+ *   out           device, bf16 [num_seqs, H_q, d]; must not alias inputs.
+ *   workspace     device, >= pa_decode_workspace_size(...) bytes, 16-byte
+ *                 aligned; may be NULL when that size is 0. Contents on entry
+ *                 are ignored; overlapping calls must not share it.
+ */
+int pa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int32_t max_blocks_per_seq,
+              const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+              float scale, void* out, void* workspace, size_t workspace_bytes,
+              const pa_desc* desc, void* stream);
+
+/*
+ * pa_decode_partitioned -- pa_decode with an explicit split-K partition of
+ * partition_blocks whole blocks per work item (0 = the library's choice,
+ * which is what pa_decode uses). The result is the same attention for any
+ * partition size up to rounding. Workspace: pa_decode_workspace_size_ex.
+ */
+int pa_decode_partitioned(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t max_context_len, float scale, void* out, void* workspace,
+                          size_t workspace_bytes, int32_t partition_blocks,
+                          const pa_desc* desc, void* stream);
+size_t pa_decode_workspace_size_ex(const pa_desc* desc, int32_t num_seqs,
+                                   int32_t max_context_len, int32_t partition_blocks);
+
+/*
+ * pa_prefill_varlen -- causal attention of a packed batch of new tokens over
+ * paged K/V. [P1 §12.6] prefill branch with prefix cache
+ * (flash_attn_varlen_func with a block table; the cu_seqlens notes).
+ *
+ * Sequence b owns queries cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (q_len of
+ * them) and k_len = cu_seqlens_k[b+1] - cu_seqlens_k[b] keys, read through
+ * block_tables[b] (cached prefix and the new tokens alike, so pa_store_kv of
+ * the new tokens runs first). Query i is the token at position
+ * k_len - q_len + i and attends to keys 0 .. k_len - q_len + i. q-head h
+ * reads kv-head h / (H_q / H_kv). fp32 accumulation, bf16 output.
+ *
+ *   q             device, bf16 [total_q, H_q, d], contiguous
+ *                 (total_q = cu_seqlens_q[num_seqs]).
+ *   cu_seqlens_q, cu_seqlens_k  device, int32 [num_seqs + 1], nondecreasing,
+ *                 starting at 0, with 0 <= q_len <= k_len per sequence.
+ *   max_seqlen_q, max_seqlen_k  host upper bounds of q_len and k_len.
+ *   block_tables  device, int32 [num_seqs, max_blocks_per_seq]; entries for
+ *                 blocks 0 .. ceil(k_len/B)-1 in [0, N).
+ *   out           device, bf16 [total_q, H_q, d].
+ */
+int pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                      int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, float scale,
+                      void* out, const pa_desc* desc, void* stream);
+
+/*
+ * pa_build_metadata -- host-side step metadata ([P5 §4]; [P2]
+ * prepare_prefill / prepare_decode). Runs on the CPU, reads host memory only.
+ *
+ * Sequence b computes positions starts[b] .. ends[b]-1 this step (decode:
+ * starts = len-1, ends = len). Writes, in batch order:
+ *   slot_mapping[...]  the slot of every computed position (two-step map),
+ *   cu_seqlens_q[b+1] = cu_seqlens_q[b] + (ends[b] - starts[b]),
+ *   cu_seqlens_k[b+1] = cu_seqlens_k[b] + ends[b]   (cached keys count).
+ *
+ *   block_tables  host, int32 [num_seqs, max_blocks_per_seq].
+ *   starts, ends  host, int32 [num_seqs], 0 <= starts <= ends,
+ *                 ceil(ends/B) <= max_blocks_per_seq, table entries for
+ *                 blocks touched >= 0 (checked: PA_ERR_INVALID_ARG).
+ *   slot_mapping  host, int32 [slot_capacity] (>= total new tokens).
+ *   cu_seqlens_q, cu_seqlens_k  host, int32 [num_seqs + 1]; either may be NULL.
+ * Returns the number of slots written (>= 0) or a PA_ERR_* code.
+ */
+int64_t pa_build_metadata(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* starts, const int32_t* ends, int32_t num_seqs,
+                          int32_t block_size, int32_t* slot_mapping, int64_t slot_capacity,
+                          int32_t* cu_seqlens_q, int32_t* cu_seqlens_k);
+
+/* Message for the last nonzero status returned on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

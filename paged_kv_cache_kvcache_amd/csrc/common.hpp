@@ -1,0 +1,80 @@
+// Shared helpers of libpa (device and host): bf16 bit handling, cross-lane
+// reductions for gfx950 wave64, argument checks and the error channel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+constexpr int kWave = 64;
+constexpr int kBlockSize = 256;  // tokens per physical block the kernels are built for
+
+// ------------------------------------------------------------------ errors
+
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Validate a descriptor; returns PA_OK or an error code (message set).
+int check_desc(const pa_desc* d);
+
+inline int launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return PA_OK;
+}
+
+// ------------------------------------------------------------- bf16 bits
+
+// bf16 -> fp32 is exact: the bf16 pattern is the top half of the fp32 one.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ------------------------------------------------------- cross-lane (DPP)
+
+// DPP controls of the GCN/CDNA "dpp_ctrl" field.
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <-> 7-i inside each 8-lane half row
+constexpr int kDppRowMirror = 0x140;      // lane i <-> 15-i inside each 16-lane row
+constexpr int kDppRowRor8 = 0x128;        // rotate a 16-lane row by 8 (= lane xor 8)
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16); every lane of a group
+// ends with the group total.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (N == 16) x += dpp<kDppRowMirror>(x);
+  return x;
+}
+
+// Lane-exact xor exchange for offsets >= 8 (whole groups of lanes swap).
+__device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask, kWave); }
+
+}  // namespace pa

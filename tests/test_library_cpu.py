@@ -1,0 +1,125 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the header
+declares, rejects bad arguments on the host, and its host metadata builder
+(slot_mapping, cu_seqlens) agrees bit for bit with the oracle."""
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_kvcache_amd import binding as B
+from paged_kv_cache_kvcache_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.lib_path()):
+        pytest.fail("libpa.so is not built: run __graft_entry__.build()")
+    return B.load()
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for required in ("pa_store_kv", "pa_decode", "pa_prefill_varlen"):
+        assert required in names
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.pa_version().decode().count(".") == 2
+
+
+def _desc(h_q=32, h_kv=8, d=128, bsz=256, n=10):
+    return B.PaDesc(h_q, h_kv, d, bsz, n)
+
+
+def test_host_argument_checks_need_no_gpu(lib):
+    d = _desc()
+    assert lib.pa_store_kv(None, 0, None, 0, None, None, None, 0, ctypes.byref(d), None) == 0
+    assert lib.pa_store_kv(None, 0, None, 0, None, None, None, 4, ctypes.byref(d), None) == \
+        B.PA_ERR_INVALID_ARG
+    assert lib.pa_store_kv(None, 0, None, 0, None, None, None, 4, None, None) == B.PA_ERR_INVALID_ARG
+    bad = _desc(h_q=30)
+    assert lib.pa_decode(None, None, None, None, 0, None, 1, 0, 1.0, None, None, 0,
+                         ctypes.byref(bad), None) == B.PA_ERR_INVALID_ARG
+    assert b"multiple" in lib.pa_last_error()
+    for kw in (dict(d=96), dict(bsz=16), dict(h_q=24, h_kv=2)):
+        assert lib.pa_decode(None, None, None, None, 0, None, 1, 0, 1.0, None, None, 0,
+                             ctypes.byref(_desc(**kw)), None) == B.PA_ERR_UNSUPPORTED
+    assert lib.pa_decode(None, None, None, None, 0, None, 0, 0, 1.0, None, None, 0,
+                         ctypes.byref(d), None) == 0  # empty batch: no-op
+    # workspace checked before any launch
+    need = lib.pa_decode_workspace_size(ctypes.byref(d), 4, 4096)
+    assert need == 4 * 32 * 16 * (128 + 2) * 4
+    assert lib.pa_decode_workspace_size(ctypes.byref(d), 4, 256) == 0
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.pa_decode(fake, fake, fake, fake, 16, fake, 4, 4096, 1.0, fake, None, 0,
+                         ctypes.byref(d), None) == B.PA_ERR_WORKSPACE
+    assert lib.pa_decode(fake, fake, fake, fake, 4, fake, 4, 4096, 1.0, fake, None, 0,
+                         ctypes.byref(d), None) == B.PA_ERR_INVALID_ARG  # table too narrow
+
+
+def test_metadata_golden_examples(lib):
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "slot_mapping_examples.json")))
+    for ex in gold["range_examples"]:
+        slots, cu_q, cu_k = B.pa_build_metadata(np.array([ex["block_table"]]), [ex["start"]],
+                                                [ex["end"]], ex["block_size"])
+        assert slots.tolist() == ex["slot_mapping"], ex["cite"]
+    for ex in gold["cu_seqlens_examples"]:
+        n = len(ex["lengths"])
+        tables = np.zeros((n, 1), dtype=np.int32)
+        _, cu_q, _ = B.pa_build_metadata(tables, [0] * n, ex["lengths"], 1 << 20)
+        assert cu_q.tolist() == ex["cu_seqlens"]
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3-0.6b", "prefill"])
+def test_metadata_matches_oracle_on_workloads(lib, name):
+    case = W.make_case(name, threads=4)
+    if isinstance(case, W.DecodeCase):
+        starts, ends = case.starts, case.context_lens
+    else:
+        starts, ends = case.starts, case.ends
+    got = B.pa_build_metadata(case.block_tables, starts, ends, case.block_size)
+    ref = oracle.build_metadata(case.block_tables, starts, ends, case.block_size)
+    for g, r in zip(got, ref):
+        assert g.dtype == np.int32 and np.array_equal(g, r)
+
+
+def test_metadata_matches_oracle_random(lib):
+    rng = np.random.default_rng(99)
+    for _ in range(50):
+        bsz = int(rng.choice([4, 16, 256]))
+        n = int(rng.integers(1, 9))
+        ends = rng.integers(0, 6 * bsz, size=n)
+        starts = (ends * rng.random(n)).astype(np.int64)
+        width = max(1, int(-(-ends.max() // bsz)))
+        tables = rng.permutation(n * width + 7)[: n * width].reshape(n, width).astype(np.int32)
+        got = B.pa_build_metadata(tables, starts, ends, bsz)
+        ref = oracle.build_metadata(tables, starts, ends, bsz)
+        for g, r in zip(got, ref):
+            assert np.array_equal(g, r)
+
+
+def test_metadata_rejects_padding_and_bad_ranges(lib):
+    tables = np.array([[3, -1]], dtype=np.int32)
+    with pytest.raises(B.PAError):
+        B.pa_build_metadata(tables, [0], [300], 256)  # position 256 hits -1 padding
+    with pytest.raises(B.PAError):
+        B.pa_build_metadata(tables, [5], [2], 256)
+    with pytest.raises(B.PAError):
+        B.pa_build_metadata(tables, [0], [600], 256)  # needs 3 blocks, table has 2
