@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+A step is one pass of the decode hot path over the Qwen3-8B-shaped batch
+(32 q / 8 kv heads, head_dim 128, block 256, 256 sequences with context
+U[512, 8192]): ``pa_store_kv`` of the 256 new tokens, then ``pa_decode``.
+Inputs are seeded synthetic data already resident in HBM when timing starts.
+
+Prints ONE JSON line: the metric (KV GB/s of the step's algorithmic bytes,
+with % of HBM peak and tokens/s beside it), the roofline of the dominant
+call (pa_decode) timed with HIP events on its stream, and the CPU oracle
+baseline on a bounded sample. ``--prefill`` adds the varlen prefill
+workload (MFMA) as an extra object.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+LAYERS_QWEN3_8B = 36
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_decode_qwen3-8b.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_kvcache_amd", "csrc", "decode.hip")
+
+
+def decode_bytes(case) -> int:
+    """Algorithmic HBM bytes of one pa_decode call: every K and V row of every
+    context token once (2 * H_kv * d * 2 bytes per token), q read and out
+    written once, one table entry per block and one length per sequence."""
+    import numpy as np
+    ctx = case.context_lens.astype(np.int64)
+    kv = int(ctx.sum()) * case.num_kv_heads * case.head_dim * 2 * 2
+    qo = 2 * case.batch * case.num_q_heads * case.head_dim * 2
+    tables = int((-(-ctx // case.block_size)).sum()) * 4
+    return kv + qo + tables + 4 * case.batch
+
+
+def store_bytes(n_tokens: int, h_kv: int, d: int) -> int:
+    """K and V rows read once and written once, plus one slot per token."""
+    return 2 * 2 * n_tokens * h_kv * d * 2 + 4 * n_tokens
+
+
+def prefill_flops(starts, ends, h_q: int, d: int) -> float:
+    """Causal-exact FLOPs: query at position p attends p+1 keys; QK^T and PV
+    each cost 2*d FLOPs per (query, key, head)."""
+    total = 0
+    for s, e in zip(starts, ends):
+        s, e = int(s), int(e)
+        total += (e * (e + 1) - s * (s + 1)) // 2  # sum over p in [s, e) of (p + 1)
+    return float(total) * h_q * 4 * d
+
+
+def src_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if it is missing or was taken on a different kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != src_hash(kernel_src):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle on the host, one thread, over the first sequences of
+    the same batch until about ``budget_s`` seconds are spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    done, tokens = 0, 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        for b in range(case.batch):
+            oracle.decode_one(case.q[b], case.k_cache, case.v_cache, case.block_tables[b],
+                              int(case.context_lens[b]), case.scale)
+            done += 1
+            tokens += int(case.context_lens[b])
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    el = time.perf_counter() - t0
+    kv = tokens * case.num_kv_heads * case.head_dim * 2 * 2
+    qo = 2 * done * case.num_q_heads * case.head_dim * 2
+    return {"value": round((kv + qo) / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "fp64 numpy oracle decode of the first %d of %d sequences (%d context "
+                      "tokens, %.1f s, 1 thread); store not included" % (
+                          done, case.batch, tokens, el),
+            "tokens_per_s_per_layer": round(done / el, 3)}
+
+
+def run_prefill(args, torch, B, W, dev):
+    import numpy as np
+    case = W.make_case("prefill")
+    slots, cu_q, cu_k = B.pa_build_metadata(case.block_tables, case.starts, case.ends,
+                                            case.block_size)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bf(a):
+        return t(a.view(np.int16)).view(torch.bfloat16)
+
+    kc, vc = bf(case.k_cache), bf(case.v_cache)
+    k_new, v_new, q = bf(case.k_new), bf(case.v_new), bf(case.q)
+    out = torch.empty_like(q)
+    slots_d, cuq_d, cuk_d, bt_d = t(slots), t(cu_q), t(cu_k), t(case.block_tables)
+    qlens = case.ends - case.starts
+    mq, mk = int(qlens.max()), int(case.ends.max())
+
+    def store():
+        B.pa_store_kv(k_new, v_new, kc, vc, slots_d)
+
+    def attn():
+        B.pa_prefill_varlen(q, kc, vc, cuq_d, cuk_d, mq, mk, bt_d, case.scale, out)
+
+    for _ in range(max(1, args.warmup)):
+        store()
+        attn()
+    torch.cuda.synchronize(dev)
+    n = max(3, args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record()
+        store()
+        ev[i][1].record()
+        attn()
+        ev[i][2].record()
+    torch.cuda.synchronize(dev)
+    t_store = sum(e[0].elapsed_time(e[1]) for e in ev) / n * 1e-3
+    t_attn = sum(e[1].elapsed_time(e[2]) for e in ev) / n * 1e-3
+    flops = prefill_flops(case.starts, case.ends, case.num_q_heads, case.head_dim)
+    sb = store_bytes(int(qlens.sum()), case.num_kv_heads, case.head_dim)
+    return {
+        "workload": "prefill: 16 prompts, shared 1024-token prefix (4 blocks) + suffix "
+                    "U[100,2000], 32 q / 8 kv heads, d 128",
+        "q_tokens": int(qlens.sum()),
+        "ms_store": round(t_store * 1e3, 4), "ms_prefill": round(t_attn * 1e3, 4),
+        "store_GBps": round(sb / t_store / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(flops / t_attn / 1e12, 2),
+                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(flops / t_attn / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "q_tokens_per_s": round(int(qlens.sum()) / (t_store + t_attn), 1),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen3-8b", choices=["qwen3-8b", "qwen3-0.6b", "long"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--prefill", action="store_true", help="also time the prefill workload")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the single-GPU path only; --gpus %d (WORLD_SIZE %d) is not "
+              "supported: this build has no multi-GPU path" % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_kvcache_amd import binding as B
+    from paged_kv_cache_kvcache_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_calibration_bytes": n, "launches": max(1, args.steps)}))
+        return 0
+
+    B.load()
+    case = W.make_case(args.config)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bf(a):
+        return t(a.view(np.int16)).view(torch.bfloat16)
+
+    slots, _, _ = B.pa_build_metadata(case.block_tables, case.starts, case.context_lens,
+                                      case.block_size)
+    kc, vc = bf(case.k_cache), bf(case.v_cache)
+    q, k_new, v_new = bf(case.q), bf(case.k_new), bf(case.v_new)
+    out = torch.empty_like(q)
+    slots_d, bt_d, ctx_d = t(slots), t(case.block_tables), t(case.context_lens)
+    max_ctx = int(case.context_lens.max())
+    ws_bytes = B.pa_decode_workspace_size(case.num_q_heads, kc, case.batch, max_ctx)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def store():
+        B.pa_store_kv(k_new, v_new, kc, vc, slots_d)
+
+    def decode():
+        B.pa_decode(q, kc, vc, bt_d, ctx_d, case.scale, out, max_context_len=max_ctx,
+                    workspace=ws)
+
+    for _ in range(args.warmup):
+        store()
+        decode()
+    torch.cuda.synchronize(dev)
+
+    # whole-step timing: K steps back to back between two events
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    start.record()
+    for _ in range(args.steps):
+        store()
+        decode()
+    end.record()
+    torch.cuda.synchronize(dev)
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # per-call durations: events around each call, on the launch stream
+    n = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    torch.cuda.synchronize(dev)
+    for i in range(n):
+        ev[i][0].record()
+        store()
+        ev[i][1].record()
+        decode()
+        ev[i][2].record()
+    torch.cuda.synchronize(dev)
+    ms_store = sum(e[0].elapsed_time(e[1]) for e in ev) / n
+    ms_decode = sum(e[1].elapsed_time(e[2]) for e in ev) / n
+
+    db = decode_bytes(case)
+    sb = store_bytes(case.batch, case.num_kv_heads, case.head_dim)
+    gbs = (db + sb) / (ms_step * 1e-3) / 1e9
+    dec_gbs = db / (ms_decode * 1e-3) / 1e9
+    traffic = traffic_from_profile(DECODE_SRC)
+
+    rec = {
+        "metric": "paged decode: KV GB/s (% HBM peak) + tokens/s at Qwen3-8B shape, batch 256",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": W.DESCRIPTIONS[args.config] + "; step = store of the batch's "
+                   "new tokens + decode, one layer", "global_batch": case.batch,
+                   "seq_len": max_ctx, "parallelism": "none (1 GPU)"},
+        "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": {"per_layer": round(case.batch / (ms_step * 1e-3), 1),
+                         "model_36_layers": round(case.batch / (LAYERS_QWEN3_8B * ms_step * 1e-3),
+                                                  1)},
+        "ms_store": round(ms_store, 5),
+        "ms_decode": round(ms_decode, 5),
+        "algorithmic_bytes": {"decode": db, "store": sb},
+        "roofline": {"bound": "hbm", "kernel": "pa_decode (split-K + merge)",
+                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+    if args.prefill:
+        rec["prefill"] = run_prefill(args, torch, B, W, dev)
+    if args.cpu_budget > 0:
+        rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

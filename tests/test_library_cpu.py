@@ -64,9 +64,16 @@ def test_host_argument_checks_need_no_gpu(lib):
     assert lib.pa_decode(None, None, None, None, 0, None, 0, 0, 1.0, None, None, 0,
                          ctypes.byref(d), None) == 0  # empty batch: no-op
     # workspace checked before any launch
-    need = lib.pa_decode_workspace_size(ctypes.byref(d), 4, 4096)
-    assert need == 4 * 32 * 16 * (128 + 2) * 4
+    # one partition of P blocks per work item: (m, l, o[d]) fp32 per
+    # (sequence, q-head, partition) when some sequence needs > 1 partition
+    for pb in (1, 2, 3):
+        parts = -(-4096 // (256 * pb))
+        assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4, 4096, pb) == \
+            4 * 32 * parts * (128 + 2) * 4
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4, 256, 1) == 0
     assert lib.pa_decode_workspace_size(ctypes.byref(d), 4, 256) == 0
+    need = lib.pa_decode_workspace_size(ctypes.byref(d), 4, 4096)
+    assert need > 0
     fake = ctypes.c_void_p(0x1000)
     assert lib.pa_decode(fake, fake, fake, fake, 16, fake, 4, 4096, 1.0, fake, None, 0,
                          ctypes.byref(d), None) == B.PA_ERR_WORKSPACE
