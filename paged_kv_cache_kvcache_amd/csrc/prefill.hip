@@ -1,10 +1,387 @@
-// pa_prefill_varlen (placeholder until the MFMA kernel lands).
+// pa_prefill_varlen: causal varlen prefill over paged K/V, bf16 MFMA on gfx950.
+//
+// What is computed ("12. 推理加速(二): nano-vllm — 1200 行手写 vLLM", §12.6,
+// prefill branch with prefix cache and the cu_seqlens notes): sequence b has
+// q_len new tokens packed at rows cu_q[b].., and k_len keys read through its
+// block table (cached prefix plus the new tokens, stored beforehand). Query i
+// sits at position k_len - q_len + i and attends to keys 0 .. that position.
+//
+// How (MI355X design):
+//   * Work item = workgroup of 4 waves for (sequence, kv-head, block of
+//     256/G query positions). Its 16 MFMA column tiles are 16 positions x 1
+//     q-head each, covering all G q-heads of the kv-head, so every K/V tile
+//     staged in LDS serves the whole GQA group.
+//   * Scores are computed transposed, S^T = K Q^T, with
+//     v_mfma_f32_16x16x32_bf16: A = K rows from LDS, B = Q held in registers
+//     for the whole loop. The accumulator layout of S^T (one query column per
+//     lane, keys down the lane groups) is exactly the B-operand layout of the
+//     next product O^T += V^T P^T once the 32 keys of a step are numbered in
+//     the order the lanes hold them, so P never goes through LDS. V is staged
+//     transposed (d-major) in LDS in that key order.
+//   * Online softmax per query column: base-2 exponent with scale*log2(e)
+//     folded in, running max exchanged across the 4 lane groups of a column,
+//     P rounded to bf16 for the MFMA, fp32 accumulation, bf16 output.
+//   * Keys are staged 64 at a time (a stage never straddles a 256-token block,
+//     so one block-table lookup per stage), double-buffered: the next stage's
+//     global loads are in flight while the current one is multiplied.
+//   * Causal work skipping: stages past the work item's last query are never
+//     loaded; a wave skips the 32-key steps that lie after all its queries;
+//     only steps that cross the diagonal apply the mask.
+//   * Grid order: per sequence the last position blocks (the most keys) come
+//     first; consecutive workgroups differ in kv-head so one (sequence,
+//     kv-head)'s blocks, which re-read the same K/V, land on the same XCD.
+#include <cmath>
+
 #include "common.hpp"
 
-extern "C" int pa_prefill_varlen(const void*, const void*, const void*, const int32_t*,
-                                 const int32_t*, int32_t, int32_t, int32_t, const int32_t*,
-                                 int32_t, float, void*, const pa_desc* desc, void*) {
-  int rc = pa::check_desc(desc);
+namespace pa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kThreads = kWaves * kWave;
+constexpr int kNT = 4;           // 16-column tiles per wave
+constexpr int kKT = 64;          // keys per LDS stage
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* block_tables;
+  uint16_t* out;
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  float scale_log2;
+};
+
+template <int D>
+struct Geo {
+  static constexpr int KROW = D * 2 + 16;    // bytes per staged K row (padded)
+  static constexpr int VROW = kKT * 2 + 16;  // bytes per staged V^T row (padded)
+  static constexpr int KBYTES = kKT * KROW;
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int KCHUNKS = kKT * D / 8 / kThreads;  // 16-byte K loads per thread
+  static constexpr int VW = D / 8;                        // V elements per thread per key
+  static constexpr int VLOADS = VW / 8;                   // 16-byte V loads per key
+};
+
+// Position of key k (0..31) of a 32-key step in the order the MFMA lanes hold
+// it: lane group j holds keys 4j..4j+3 (first 16-key tile) then 16+4j..16+4j+3.
+__device__ __forceinline__ int key_slot(int k) {
+  return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
+}
+
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
+
+template <int D>
+__device__ __forceinline__ void load_stage(const PrefillArgs& a, const int32_t* bt, int g, int kmax,
+                                           int stage, u32x4 (&kreg)[Geo<D>::KCHUNKS],
+                                           u32x4 (&vreg)[2][Geo<D>::VLOADS]) {
+  using GG = Geo<D>;
+  const int t = threadIdx.x;
+  const int kbase = stage * kKT;
+  const int blk_raw = bt[kbase / kBlockSize];
+  const int64_t blk = (blk_raw >= 0 && blk_raw < a.num_blocks) ? blk_raw : 0;
+  const int64_t row_elems = (int64_t)a.num_kv_heads * D;
+  // keys at or past kmax are never visible; re-read the last needed one
+  const uint16_t* kb = a.k_cache + (blk * kBlockSize) * row_elems + (int64_t)g * D;
+  const uint16_t* vb = a.v_cache + (blk * kBlockSize) * row_elems + (int64_t)g * D;
+#pragma unroll
+  for (int i = 0; i < GG::KCHUNKS; ++i) {
+    const int c = t + i * kThreads;
+    const int key = c / (D / 8);
+    const int ch = c % (D / 8);
+    const int kp = min(kbase + key, kmax - 1) % kBlockSize;
+    kreg[i] = *reinterpret_cast<const u32x4*>(kb + kp * row_elems + ch * 8);
+  }
+  const int pair = t % 32;  // keys 2*pair, 2*pair+1 of the stage
+  const int dg = t / 32;    // d range [dg*VW, dg*VW+VW)
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int kp = min(kbase + 2 * pair + s, kmax - 1) % kBlockSize;
+#pragma unroll
+    for (int i = 0; i < GG::VLOADS; ++i)
+      vreg[s][i] = *reinterpret_cast<const u32x4*>(vb + kp * row_elems + dg * GG::VW + i * 8);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_stage(char* lds, const u32x4 (&kreg)[Geo<D>::KCHUNKS],
+                                            const u32x4 (&vreg)[2][Geo<D>::VLOADS]) {
+  using GG = Geo<D>;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < GG::KCHUNKS; ++i) {
+    const int c = t + i * kThreads;
+    const int key = c / (D / 8);
+    const int ch = c % (D / 8);
+    *reinterpret_cast<u32x4*>(lds + key * GG::KROW + ch * 16) = kreg[i];
+  }
+  // V^T[d][slot]: a dword holds the pair (V[2p][d], V[2p+1][d]); an even key
+  // and its odd neighbour occupy adjacent slots
+  const int pair = t % 32;
+  const int dg = t / 32;
+  const int key0 = 2 * pair;
+  const int slot = (key0 / 32) * 32 + key_slot(key0 % 32);
+  char* vt = lds + GG::KBYTES + slot * 2;
+#pragma unroll
+  for (int i = 0; i < GG::VLOADS; ++i) {
+    const uint32_t lo[4] = {vreg[0][i].x, vreg[0][i].y, vreg[0][i].z, vreg[0][i].w};
+    const uint32_t hi[4] = {vreg[1][i].x, vreg[1][i].y, vreg[1][i].z, vreg[1][i].w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int d = dg * GG::VW + i * 8 + 2 * w;
+      // element d: low halves; element d+1: high halves
+      const uint32_t e0 = __builtin_amdgcn_perm(hi[w], lo[w], 0x05040100u);
+      const uint32_t e1 = __builtin_amdgcn_perm(hi[w], lo[w], 0x07060302u);
+      *reinterpret_cast<uint32_t*>(vt + d * GG::VROW) = e0;
+      *reinterpret_cast<uint32_t*>(vt + (d + 1) * GG::VROW) = e1;
+    }
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+  using GG = Geo<D>;
+  constexpr int QB = 16 * kNT * kWaves / G;  // query positions per workgroup
+  constexpr int KSTEPS = D / 32;             // MFMA k-steps over head_dim
+  constexpr int MT = D / 16;                 // 16-row tiles of O^T over head_dim
+  __shared__ __attribute__((aligned(16))) char lds[2 * GG::STAGE];
+
+  const int H_kv = a.num_kv_heads;
+  const int H_q = H_kv * G;
+  int idx = blockIdx.x;
+  const int g = idx % H_kv;
+  idx /= H_kv;
+  const int b = idx % a.num_seqs;
+  const int r = idx / a.num_seqs;  // position block counted from the end
+
+  const int q0 = a.cu_q[b];
+  const int q_len = a.cu_q[b + 1] - q0;
+  int k_len = a.cu_k[b + 1] - a.cu_k[b];
+  k_len = min(k_len, a.max_blocks * kBlockSize);
+  if (q_len <= 0 || k_len < q_len) return;  // nothing to do / broken precondition
+  const int p_end = q_len - r * QB;         // positions [p_end - QB, p_end)
+  if (p_end <= 0) return;
+  const int p0 = p_end - QB;
+  const int off = k_len - q_len;  // query i is the token at position off + i
+  const int kmax = off + p_end;   // keys this workgroup can see: [0, kmax)
+  const int n_stages = (kmax + kKT - 1) / kKT;
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
+
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int col = lane % 16;
+  const int grp = lane / 16;
+
+  int head[kNT], pbase[kNT];
+  int wmax = -1;  // last position any column of this wave holds
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) {
+    const int T = wave * kNT + j;
+    head[j] = g * G + T % G;
+    pbase[j] = p0 + (T / G) * 16;
+    wmax = max(wmax, pbase[j] + 15);
+  }
+  wmax = min(wmax, p_end - 1);
+
+  // Q^T operands for all k-steps (rows outside the sequence re-read row 0;
+  // their columns are never written)
+  bf16x8 qf[kNT][KSTEPS];
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) {
+    const int pos = max(pbase[j] + col, 0);
+    const uint16_t* qp = a.q + ((int64_t)(q0 + pos) * H_q + head[j]) * D + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      qf[j][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 32));
+  }
+
+  f32x4 o[kNT][MT];
+  float m[kNT], l[kNT];
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  u32x4 kreg[GG::KCHUNKS];
+  u32x4 vreg[2][GG::VLOADS];
+  load_stage<D>(a, bt, g, kmax, 0, kreg, vreg);
+  store_stage<D>(lds, kreg, vreg);
+  __syncthreads();
+
+  for (int st = 0; st < n_stages; ++st) {
+    const bool more = st + 1 < n_stages;
+    if (more) load_stage<D>(a, bt, g, kmax, st + 1, kreg, vreg);
+    const char* ks_lds = lds + (st & 1) * GG::STAGE;
+    const char* vt_lds = ks_lds + GG::KBYTES;
+
+#pragma unroll
+    for (int sub = 0; sub < kKT / 32; ++sub) {
+      const int key0 = st * kKT + sub * 32;  // absolute position of the step's first key
+      if (key0 > off + wmax) continue;       // every key is after every query of the wave
+      // ---- S^T = K Q^T for 32 keys x (kNT x 16) columns
+      f32x4 s[2][kNT];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int j = 0; j < kNT; ++j) s[kt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const char* arow = ks_lds + (sub * 32 + kt * 16 + col) * GG::KROW + grp * 16;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + ks * 64));
+#pragma unroll
+          for (int j = 0; j < kNT; ++j)
+            s[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[j][ks], s[kt][j], 0, 0, 0);
+        }
+      }
+      // ---- online softmax per column; build P^T operands
+      bf16x8 pf[kNT];
+#pragma unroll
+      for (int j = 0; j < kNT; ++j) {
+        const int qpos = off + pbase[j] + col;  // absolute position of this column's query
+        float sv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = s[0][j][i];
+          sv[4 + i] = s[1][j][i];
+        }
+        if (key0 + 31 > off + pbase[j]) {  // the step crosses some column's diagonal
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int kpos = key0 + (i >> 2) * 16 + grp * 4 + (i & 3);
+            if (kpos > qpos) sv[i] = -INFINITY;
+          }
+        }
+        float mx = sv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+        mx = fmaxf(mx, xor_lane(mx, 16));
+        mx = fmaxf(mx, xor_lane(mx, 32));
+        const float mnew = fmaxf(m[j], mx * a.scale_log2);
+        const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m[j] - msafe);
+        m[j] = mnew;
+        l[j] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[j][mt] *= alpha;
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], a.scale_log2, -msafe));
+          l[j] += p[i];
+        }
+        uint4 pk;
+        pk.x = pack2_bf16(p[0], p[1]);
+        pk.y = pack2_bf16(p[2], p[3]);
+        pk.z = pack2_bf16(p[4], p[5]);
+        pk.w = pack2_bf16(p[6], p[7]);
+        pf[j] = __builtin_bit_cast(bf16x8, pk);
+      }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const char* vrow = vt_lds + (mt * 16 + col) * GG::VROW + (sub * 32 + grp * 8) * 2;
+        const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vrow));
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+          o[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf[j], o[j][mt], 0, 0, 0);
+      }
+    }
+
+    if (more) store_stage<D>(lds + ((st + 1) & 1) * GG::STAGE, kreg, vreg);
+    __syncthreads();
+  }
+
+  // ---- epilogue: column sums across the 4 lane groups, normalise, store
+#pragma unroll
+  for (int j = 0; j < kNT; ++j) {
+    float lt = l[j];
+    lt += xor_lane(lt, 16);
+    lt += xor_lane(lt, 32);
+    const int pos = pbase[j] + col;
+    if (pos < 0 || pos >= p_end) continue;
+    const float inv = 1.f / lt;
+    uint16_t* dst = a.out + ((int64_t)(q0 + pos) * H_q + head[j]) * D + grp * 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      uint2 v;
+      v.x = pack_bf16x2(o[j][mt][0] * inv, o[j][mt][1] * inv);
+      v.y = pack_bf16x2(o[j][mt][2] * inv, o[j][mt][3] * inv);
+      *reinterpret_cast<uint2*>(dst + mt * 16) = v;
+    }
+  }
+}
+
+using PrefillFn = void (*)(PrefillArgs);
+
+template <int D>
+PrefillFn pick(int G) {
+  switch (G) {
+    case 1: return prefill_kernel<D, 1>;
+    case 2: return prefill_kernel<D, 2>;
+    case 4: return prefill_kernel<D, 4>;
+    case 8: return prefill_kernel<D, 8>;
+  }
+  return nullptr;
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 float scale, void* out, const pa_desc* desc, void* stream) {
+  using namespace pa;
+  int rc = check_desc(desc);
   if (rc) return rc;
-  return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill_varlen: not built yet");
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_blocks_per_seq < 0)
+    return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: negative size");
+  if (num_seqs == 0 || max_seqlen_q == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_tables || !out)
+    return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: NULL pointer");
+  if (max_seqlen_q > max_seqlen_k)
+    return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: max_seqlen_q %d > max_seqlen_k %d",
+                max_seqlen_q, max_seqlen_k);
+  if ((int64_t)max_blocks_per_seq * kBlockSize < max_seqlen_k)
+    return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: max_seqlen_k %d exceeds %d table entries",
+                max_seqlen_k, max_blocks_per_seq);
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15u)
+    return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: q, caches and out must be 16-byte aligned");
+  const int G = desc->num_q_heads / desc->num_kv_heads;
+  const int D = desc->head_dim;
+  const int QB = 16 * kNT * kWaves / G;
+  const int64_t blocks = (int64_t)num_seqs * desc->num_kv_heads * ((max_seqlen_q + QB - 1) / QB);
+  if (blocks > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: grid too large");
+
+  PrefillArgs a;
+  a.q = (const uint16_t*)q;
+  a.k_cache = (const uint16_t*)k_cache;
+  a.v_cache = (const uint16_t*)v_cache;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.block_tables = block_tables;
+  a.out = (uint16_t*)out;
+  a.num_blocks = desc->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.scale_log2 = scale * kLog2e;
+  PrefillFn fn = D == 128 ? pick<128>(G) : pick<64>(G);
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a);
+  return launch_status("pa_prefill_varlen");
 }

@@ -1,0 +1,148 @@
+"""GPU parity: pa_prefill_varlen (after pa_store_kv of the new tokens) vs the
+fp64 oracle, max-abs 1e-2 / mean-abs 1e-3, through the C-ABI library."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import assert_close, dev_bf16, dev_i32, host_bits, host_f64, poison_unused
+from paged_kv_cache_kvcache_amd import binding as B
+from paged_kv_cache_kvcache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+
+
+def run_prefill_step(case, poison=False):
+    print("prefill step: %s batch=%d H=%d/%d d=%d q_tokens=%d poison=%s" % (
+        case.name, case.batch, case.num_q_heads, case.num_kv_heads, case.head_dim,
+        int((case.ends - case.starts).sum()), poison), flush=True)
+    slots, cu_q, cu_k = B.pa_build_metadata(case.block_tables, case.starts, case.ends,
+                                            case.block_size)
+    kc0, vc0 = case.k_cache, case.v_cache
+    if poison:  # only cached positions hold data; the new tokens' rows are NaN
+        kc0, vc0 = poison_unused(kc0, vc0, case.block_tables, case.starts, case.block_size)
+    kc, vc = dev_bf16(kc0), dev_bf16(vc0)
+    B.pa_store_kv(dev_bf16(case.k_new), dev_bf16(case.v_new), kc, vc, dev_i32(slots))
+    q = dev_bf16(case.q)
+    out = torch.empty_like(q)
+    qlens = case.ends - case.starts
+    B.pa_prefill_varlen(q, kc, vc, dev_i32(cu_q), dev_i32(cu_k), int(qlens.max()),
+                        int(case.ends.max()), dev_i32(case.block_tables), case.scale, out)
+    torch.cuda.synchronize()
+    kref, vref = oracle.store_kv(kc0, vc0, case.k_new, case.v_new, slots)
+    assert np.array_equal(host_bits(kc), kref) and np.array_equal(host_bits(vc), vref)
+    return host_f64(out), kref, vref, cu_q, cu_k
+
+
+def test_prefix_cached_workload_sampled():
+    """16 prompts sharing a 1024-token prefix (4 blocks) + suffix U[100, 2000];
+    every sequence is checked on its first, last and 24 random query rows."""
+    case = W.make_case("prefill")
+    out, kref, vref, cu_q, cu_k = run_prefill_step(case)
+    rng = np.random.default_rng(3)
+    got, ref = [], []
+    for b in range(case.batch):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        n = q1 - q0
+        rows = sorted(set([0, 1, 15, 16, n - 1, n - 2]) | set(rng.integers(0, n, 24).tolist()))
+        r = oracle.prefill_one(case.q[q0:q1], kref, vref, case.block_tables[b],
+                               int(case.ends[b]), case.scale, query_rows=rows)
+        got.append(out[q0:q1][rows])
+        ref.append(r[rows])
+    mx, mean = assert_close(np.concatenate(got), np.concatenate(ref), "prefill workload")
+    print("  parity prefill workload: max abs %.3g mean abs %.3g" % (mx, mean))
+
+
+def ragged_case(h_q, h_kv, d, prefix, suffix, seed):
+    """Own (unshared) blocks per sequence; cached prefixes of any length."""
+    rng = np.random.default_rng(seed)
+    starts = np.array(prefix, dtype=np.int32)
+    ends = starts + np.array(suffix, dtype=np.int32)
+    need = [-(-int(e) // 256) for e in ends]
+    nb = int(np.ceil(1.1 * sum(need)))
+    perm = rng.permutation(nb)
+    tables, pos = [], 0
+    for n in need:
+        tables.append(perm[pos:pos + n].tolist())
+        pos += n
+    total = int(sum(suffix))
+    return W.PrefillCase("ragged", h_q, h_kv, d, 256, nb,
+                         W.normal_bf16(rng, (total, h_q, d)),
+                         W.normal_bf16(rng, (total, h_kv, d)),
+                         W.normal_bf16(rng, (total, h_kv, d)),
+                         W.normal_bf16(rng, (nb, 256, h_kv, d)),
+                         W.normal_bf16(rng, (nb, 256, h_kv, d)),
+                         W.pad_tables(tables), starts, ends, 1.0 / np.sqrt(d), seed)
+
+
+@pytest.mark.parametrize("h_q,h_kv,d", [(32, 8, 128), (8, 8, 128), (16, 8, 128), (64, 8, 128),
+                                         (4, 2, 64), (8, 1, 64), (16, 2, 64)])
+def test_small_cases_full_oracle(h_q, h_kv, d):
+    """Ragged q lengths (1, < 16, not multiples of the tile), cached prefixes
+    that end mid-block (chunked prefill), no prefix, poisoned unused rows."""
+    prefix = [0, 3, 256, 300, 511, 700]
+    suffix = [70, 1, 15, 129, 2, 300]
+    case = ragged_case(h_q, h_kv, d, prefix, suffix, seed=81 + h_q + d)
+    out, kref, vref, cu_q, cu_k = run_prefill_step(case, poison=True)
+    ref = oracle.prefill_varlen(case.q, kref, vref, cu_q, cu_k, case.block_tables, case.scale)
+    mx, mean = assert_close(out, ref, "small prefill %d/%d/%d" % (h_q, h_kv, d))
+    print("  parity: max abs %.3g mean abs %.3g" % (mx, mean))
+
+
+def test_prefill_with_one_query_matches_decode():
+    """q_len = 1 per sequence: the prefill path computes the decode result."""
+    lens = [1, 17, 256, 300, 1000, 4097]
+    case = W.decode_case(32, 8, 128, lens, seed=91)
+    slots, cu_q, cu_k = B.pa_build_metadata(case.block_tables, case.starts, case.context_lens, 256)
+    kc, vc = dev_bf16(case.k_cache), dev_bf16(case.v_cache)
+    B.pa_store_kv(dev_bf16(case.k_new), dev_bf16(case.v_new), kc, vc, dev_i32(slots))
+    q = dev_bf16(case.q)
+    out_p = torch.empty_like(q)
+    out_d = torch.empty_like(q)
+    B.pa_prefill_varlen(q, kc, vc, dev_i32(cu_q), dev_i32(cu_k), 1, max(lens),
+                        dev_i32(case.block_tables), case.scale, out_p)
+    B.pa_decode(q, kc, vc, dev_i32(case.block_tables), dev_i32(case.context_lens), case.scale,
+                out_d, max_context_len=max(lens))
+    torch.cuda.synchronize()
+    kref, vref = oracle.store_kv(case.k_cache, case.v_cache, case.k_new, case.v_new, slots)
+    ref = oracle.decode(case.q, kref, vref, case.block_tables, case.context_lens, case.scale)
+    assert_close(host_f64(out_p), ref, "prefill q_len=1")
+    assert_close(host_f64(out_d), ref, "decode")
+
+
+def test_full_prompt_without_cache_shares_prefix_rows():
+    """Two prompts that share their first 512 tokens' blocks and queries,
+    prefilled from position 0: their first 512 output rows are identical."""
+    rng = np.random.default_rng(92)
+    h_q, h_kv, d = 32, 8, 128
+    case = W.prefill_case(h_q, h_kv, d, 512, [100, 400], seed=93)
+    case.starts[:] = 0
+    prefix_q = W.normal_bf16(rng, (512, h_q, d))
+    q_parts, k_parts, v_parts = [], [], []
+    prefix_k = W.normal_bf16(rng, (512, h_kv, d))
+    prefix_v = W.normal_bf16(rng, (512, h_kv, d))
+    for e in case.ends.tolist():
+        q_parts.append(np.concatenate([prefix_q, W.normal_bf16(rng, (e - 512, h_q, d))]))
+        k_parts.append(np.concatenate([prefix_k, W.normal_bf16(rng, (e - 512, h_kv, d))]))
+        v_parts.append(np.concatenate([prefix_v, W.normal_bf16(rng, (e - 512, h_kv, d))]))
+    case.q = np.concatenate(q_parts)
+    case.k_new = np.concatenate(k_parts)
+    case.v_new = np.concatenate(v_parts)
+    # both sequences write the shared prefix rows with identical values, so
+    # the store's duplicate slots carry equal data
+    out, kref, vref, cu_q, cu_k = run_prefill_step(case)
+    a = out[cu_q[0]:cu_q[0] + 512]
+    b = out[cu_q[1]:cu_q[1] + 512]
+    assert np.array_equal(a, b)
+    ref = oracle.prefill_varlen(case.q, kref, vref, cu_q, cu_k, case.block_tables, case.scale,
+                                seqs=[0])
+    assert_close(out[cu_q[0]:cu_q[1]], ref[cu_q[0]:cu_q[1]], "full prompt")
