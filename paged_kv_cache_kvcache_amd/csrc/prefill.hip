@@ -22,8 +22,8 @@
 //     folded in, running max exchanged across the 4 lane groups of a column,
 //     P rounded to bf16 for the MFMA, fp32 accumulation, bf16 output.
 //   * Keys are staged 64 at a time (a stage never straddles a 256-token block,
-//     so one block-table lookup per stage), double-buffered: the next stage's
-//     global loads are in flight while the current one is multiplied.
+//     so one block-table lookup per stage), double-buffered in LDS with
+//     register staging two stages ahead of the multiply.
 //   * Causal work skipping: stages past the work item's last query are never
 //     loaded; a wave skips the 32-key steps that lie after all its queries;
 //     only steps that cross the diagonal apply the mask.
@@ -42,9 +42,22 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWaves = 4;        // waves per workgroup
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8
+#endif
+#ifndef PA_PREFILL_NT
+#define PA_PREFILL_NT 2
+#endif
+#ifndef PA_PREFILL_LAZY
+#define PA_PREFILL_LAZY 1
+#endif
+constexpr int kWaves = PA_PREFILL_WAVES;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
-constexpr int kNT = 4;           // 16-column tiles per wave
+constexpr int kNT = PA_PREFILL_NT;        // 16-column tiles per wave
+constexpr int kCols = 16 * kNT * kWaves;  // (position, q-head) columns per workgroup
+// Lazy rescaling: a column's reference max moves only when a score exceeds
+// it by more than 2^kLazyLog2 (weights stay <= 256, well inside bf16/fp32).
+constexpr float kLazyLog2 = 8.f;
 constexpr int kKT = 64;          // keys per LDS stage
 
 struct PrefillArgs {
@@ -70,9 +83,15 @@ struct Geo {
   static constexpr int VBYTES = D * VROW;
   static constexpr int STAGE = KBYTES + VBYTES;
   static constexpr int KCHUNKS = kKT * D / 8 / kThreads;  // 16-byte K loads per thread
-  static constexpr int VW = D / 8;                        // V elements per thread per key
-  static constexpr int VLOADS = VW / 8;                   // 16-byte V loads per key
+  static constexpr int VGROUPS = kThreads / 32;           // d ranges per key pair
+  static constexpr int VW = D / VGROUPS;                  // V elements per thread per key
+  static_assert(KCHUNKS >= 1 && (VW == 4 || VW == 8 || VW == 16), "stage split");
 };
+
+template <int VW> struct VVec;
+template <> struct VVec<4> { typedef __attribute__((ext_vector_type(2))) unsigned int T; };
+template <> struct VVec<8> { typedef __attribute__((ext_vector_type(4))) unsigned int T; };
+template <> struct VVec<16> { typedef __attribute__((ext_vector_type(8))) unsigned int T; };
 
 // Position of key k (0..31) of a 32-key step in the order the MFMA lanes hold
 // it: lane group j holds keys 4j..4j+3 (first 16-key tile) then 16+4j..16+4j+3.
@@ -80,12 +99,17 @@ __device__ __forceinline__ int key_slot(int k) {
   return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
 }
 
-__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
+// Two fp32 -> packed bf16 (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
 
 template <int D>
 __device__ __forceinline__ void load_stage(const PrefillArgs& a, const int32_t* bt, int g, int kmax,
                                            int stage, u32x4 (&kreg)[Geo<D>::KCHUNKS],
-                                           u32x4 (&vreg)[2][Geo<D>::VLOADS]) {
+                                           typename VVec<Geo<D>::VW>::T (&vreg)[2]) {
   using GG = Geo<D>;
   const int t = threadIdx.x;
   const int kbase = stage * kKT;
@@ -103,20 +127,19 @@ __device__ __forceinline__ void load_stage(const PrefillArgs& a, const int32_t* 
     const int kp = min(kbase + key, kmax - 1) % kBlockSize;
     kreg[i] = *reinterpret_cast<const u32x4*>(kb + kp * row_elems + ch * 8);
   }
+  typedef typename VVec<GG::VW>::T VT;
   const int pair = t % 32;  // keys 2*pair, 2*pair+1 of the stage
   const int dg = t / 32;    // d range [dg*VW, dg*VW+VW)
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int kp = min(kbase + 2 * pair + s, kmax - 1) % kBlockSize;
-#pragma unroll
-    for (int i = 0; i < GG::VLOADS; ++i)
-      vreg[s][i] = *reinterpret_cast<const u32x4*>(vb + kp * row_elems + dg * GG::VW + i * 8);
+    vreg[s] = *reinterpret_cast<const VT*>(vb + kp * row_elems + dg * GG::VW);
   }
 }
 
 template <int D>
 __device__ __forceinline__ void store_stage(char* lds, const u32x4 (&kreg)[Geo<D>::KCHUNKS],
-                                            const u32x4 (&vreg)[2][Geo<D>::VLOADS]) {
+                                            const typename VVec<Geo<D>::VW>::T (&vreg)[2]) {
   using GG = Geo<D>;
   const int t = threadIdx.x;
 #pragma unroll
@@ -134,25 +157,20 @@ __device__ __forceinline__ void store_stage(char* lds, const u32x4 (&kreg)[Geo<D
   const int slot = (key0 / 32) * 32 + key_slot(key0 % 32);
   char* vt = lds + GG::KBYTES + slot * 2;
 #pragma unroll
-  for (int i = 0; i < GG::VLOADS; ++i) {
-    const uint32_t lo[4] = {vreg[0][i].x, vreg[0][i].y, vreg[0][i].z, vreg[0][i].w};
-    const uint32_t hi[4] = {vreg[1][i].x, vreg[1][i].y, vreg[1][i].z, vreg[1][i].w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int d = dg * GG::VW + i * 8 + 2 * w;
-      // element d: low halves; element d+1: high halves
-      const uint32_t e0 = __builtin_amdgcn_perm(hi[w], lo[w], 0x05040100u);
-      const uint32_t e1 = __builtin_amdgcn_perm(hi[w], lo[w], 0x07060302u);
-      *reinterpret_cast<uint32_t*>(vt + d * GG::VROW) = e0;
-      *reinterpret_cast<uint32_t*>(vt + (d + 1) * GG::VROW) = e1;
-    }
+  for (int w = 0; w < GG::VW / 2; ++w) {
+    const int d = dg * GG::VW + 2 * w;
+    // element d: low halves; element d+1: high halves
+    const uint32_t e0 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
+    const uint32_t e1 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
+    *reinterpret_cast<uint32_t*>(vt + d * GG::VROW) = e0;
+    *reinterpret_cast<uint32_t*>(vt + (d + 1) * GG::VROW) = e1;
   }
 }
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   using GG = Geo<D>;
-  constexpr int QB = 16 * kNT * kWaves / G;  // query positions per workgroup
+  constexpr int QB = kCols / G;              // query positions per workgroup
   constexpr int KSTEPS = D / 32;             // MFMA k-steps over head_dim
   constexpr int MT = D / 16;                 // 16-row tiles of O^T over head_dim
   __shared__ __attribute__((aligned(16))) char lds[2 * GG::STAGE];
@@ -216,93 +234,114 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     for (int mt = 0; mt < MT; ++mt) o[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  u32x4 kreg[GG::KCHUNKS];
-  u32x4 vreg[2][GG::VLOADS];
-  load_stage<D>(a, bt, g, kmax, 0, kreg, vreg);
-  store_stage<D>(lds, kreg, vreg);
+  // Register staging two stages deep: while stage st is multiplied, stage
+  // st+1 (issued an iteration earlier) lands and stage st+2 is issued. Stage
+  // indices are clamped, so every issue is unconditional and the memory
+  // counter waits stay static.
+  u32x4 kra[GG::KCHUNKS], krb[GG::KCHUNKS];
+  typename VVec<GG::VW>::T vra[2], vrb[2];
+  load_stage<D>(a, bt, g, kmax, 0, kra, vra);
+  store_stage<D>(lds, kra, vra);
+  load_stage<D>(a, bt, g, kmax, min(1, n_stages - 1), kra, vra);
   __syncthreads();
 
-  for (int st = 0; st < n_stages; ++st) {
-    const bool more = st + 1 < n_stages;
-    if (more) load_stage<D>(a, bt, g, kmax, st + 1, kreg, vreg);
-    const char* ks_lds = lds + (st & 1) * GG::STAGE;
-    const char* vt_lds = ks_lds + GG::KBYTES;
+  // One stage: issue the loads of stage st+2 into `next`, multiply the LDS
+  // copy of stage st, then copy `ready` (stage st+1) into the other buffer.
+  auto stage_step = [&](int st, const u32x4 (&kready)[GG::KCHUNKS],
+                        const typename VVec<GG::VW>::T (&vready)[2], u32x4 (&knext)[GG::KCHUNKS],
+                        typename VVec<GG::VW>::T (&vnext)[2]) {
+    load_stage<D>(a, bt, g, kmax, min(st + 2, n_stages - 1), knext, vnext);
+      const char* ks_lds = lds + (st & 1) * GG::STAGE;
+      const char* vt_lds = ks_lds + GG::KBYTES;
 
 #pragma unroll
-    for (int sub = 0; sub < kKT / 32; ++sub) {
-      const int key0 = st * kKT + sub * 32;  // absolute position of the step's first key
-      if (key0 > off + wmax) continue;       // every key is after every query of the wave
-      // ---- S^T = K Q^T for 32 keys x (kNT x 16) columns
-      f32x4 s[2][kNT];
+      for (int sub = 0; sub < kKT / 32; ++sub) {
+        const int key0 = st * kKT + sub * 32;  // absolute position of the step's first key
+        if (key0 > off + wmax) continue;       // every key is after every query of the wave
+        // ---- S^T = K Q^T for 32 keys x (kNT x 16) columns
+        f32x4 s[2][kNT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) s[kt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const char* arow = ks_lds + (sub * 32 + kt * 16 + col) * GG::KROW + grp * 16;
+          for (int j = 0; j < kNT; ++j) s[kt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const char* arow = ks_lds + (sub * 32 + kt * 16 + col) * GG::KROW + grp * 16;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + ks * 64));
+          for (int ks = 0; ks < KSTEPS; ++ks) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + ks * 64));
 #pragma unroll
-          for (int j = 0; j < kNT; ++j)
-            s[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[j][ks], s[kt][j], 0, 0, 0);
-        }
-      }
-      // ---- online softmax per column; build P^T operands
-      bf16x8 pf[kNT];
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) {
-        const int qpos = off + pbase[j] + col;  // absolute position of this column's query
-        float sv[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[i] = s[0][j][i];
-          sv[4 + i] = s[1][j][i];
-        }
-        if (key0 + 31 > off + pbase[j]) {  // the step crosses some column's diagonal
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int kpos = key0 + (i >> 2) * 16 + grp * 4 + (i & 3);
-            if (kpos > qpos) sv[i] = -INFINITY;
+            for (int j = 0; j < kNT; ++j)
+              s[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[j][ks], s[kt][j], 0, 0, 0);
           }
         }
-        float mx = sv[0];
+        // ---- online softmax per column; build P^T operands
+        bf16x8 pf[kNT];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-        mx = fmaxf(mx, xor_lane(mx, 16));
-        mx = fmaxf(mx, xor_lane(mx, 32));
-        const float mnew = fmaxf(m[j], mx * a.scale_log2);
-        const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m[j] - msafe);
-        m[j] = mnew;
-        l[j] *= alpha;
+        for (int j = 0; j < kNT; ++j) {
+          const int qpos = off + pbase[j] + col;  // absolute position of this column's query
+          float sv[8];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) o[j][mt] *= alpha;
-        float p[8];
+          for (int i = 0; i < 4; ++i) {
+            sv[i] = s[0][j][i];
+            sv[4 + i] = s[1][j][i];
+          }
+          if (key0 + 31 > off + pbase[j]) {  // the step crosses some column's diagonal
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], a.scale_log2, -msafe));
-          l[j] += p[i];
+            for (int i = 0; i < 8; ++i) {
+              const int kpos = key0 + (i >> 2) * 16 + grp * 4 + (i & 3);
+              if (kpos > qpos) sv[i] = -INFINITY;
+            }
+          }
+          float mx = sv[0];
+#pragma unroll
+          for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+          mx = fmaxf(mx, xor_lane(mx, 16));
+          mx = fmaxf(mx, xor_lane(mx, 32));
+          mx *= a.scale_log2;
+#if PA_PREFILL_LAZY
+          // all lanes of a column see the same mx and m, so they agree on it
+          if (mx > m[j] + kLazyLog2) {
+#else
+          {
+#endif
+            const float mnew = fmaxf(m[j], mx);
+            const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);  // 0 on the first step
+            m[j] = mnew;
+            l[j] *= alpha;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) o[j][mt] *= alpha;
+          }
+          const float msafe = (m[j] == -INFINITY) ? 0.f : m[j];
+          float p[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], a.scale_log2, -msafe));
+            l[j] += p[i];
+          }
+          uint4 pk;
+          pk.x = pack2_bf16(p[0], p[1]);
+          pk.y = pack2_bf16(p[2], p[3]);
+          pk.z = pack2_bf16(p[4], p[5]);
+          pk.w = pack2_bf16(p[6], p[7]);
+          pf[j] = __builtin_bit_cast(bf16x8, pk);
         }
-        uint4 pk;
-        pk.x = pack2_bf16(p[0], p[1]);
-        pk.y = pack2_bf16(p[2], p[3]);
-        pk.z = pack2_bf16(p[4], p[5]);
-        pk.w = pack2_bf16(p[6], p[7]);
-        pf[j] = __builtin_bit_cast(bf16x8, pk);
-      }
-      // ---- O^T += V^T P^T
+        // ---- O^T += V^T P^T
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const char* vrow = vt_lds + (mt * 16 + col) * GG::VROW + (sub * 32 + grp * 8) * 2;
-        const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vrow));
+        for (int mt = 0; mt < MT; ++mt) {
+          const char* vrow = vt_lds + (mt * 16 + col) * GG::VROW + (sub * 32 + grp * 8) * 2;
+          const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vrow));
 #pragma unroll
-        for (int j = 0; j < kNT; ++j)
-          o[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf[j], o[j][mt], 0, 0, 0);
+          for (int j = 0; j < kNT; ++j)
+            o[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf[j], o[j][mt], 0, 0, 0);
+        }
       }
-    }
 
-    if (more) store_stage<D>(lds + ((st + 1) & 1) * GG::STAGE, kreg, vreg);
+    if (st + 1 < n_stages) store_stage<D>(lds + ((st + 1) & 1) * GG::STAGE, kready, vready);
     __syncthreads();
+  };
+  for (int st = 0; st < n_stages; st += 2) {
+    stage_step(st, kra, vra, krb, vrb);
+    if (st + 1 >= n_stages) break;
+    stage_step(st + 1, krb, vrb, kra, vra);
   }
 
   // ---- epilogue: column sums across the 4 lane groups, normalise, store
