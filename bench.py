@@ -65,15 +65,16 @@ def src_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_src: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if it is missing or was taken on a different kernel source."""
+def traffic_from_profile(kernel_src: str, mode: str):
+    """HBM bytes per launch of the dominant call from the committed rocprofv3
+    counter summary, or None if it is missing, was taken for another step
+    mode, or on a different kernel source."""
     try:
         with open(PMC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != src_hash(kernel_src):
+    if rec.get("source_sha256_16") != src_hash(kernel_src) or rec.get("step_mode") != mode:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -170,6 +171,11 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--prefill", action="store_true", help="also time the prefill workload")
+    ap.add_argument("--mode", default="separate", choices=["fused", "separate"],
+                    help="fused: pa_decode_step (store + decode in one pass); separate: "
+                         "pa_store_kv then pa_decode")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step in a HIP graph and time its replays")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -225,41 +231,74 @@ def main() -> int:
         B.pa_decode(q, kc, vc, bt_d, ctx_d, case.scale, out, max_context_len=max_ctx,
                     workspace=ws)
 
+    def fused():
+        B.pa_decode_step(q, k_new, v_new, kc, vc, slots_d, bt_d, ctx_d, case.scale, out,
+                         max_context_len=max_ctx, workspace=ws)
+
+    if args.mode == "fused":
+        calls = [("pa_decode_step", fused)]
+    else:
+        calls = [("pa_store_kv", store), ("pa_decode", decode)]
+
+    def step():
+        for _, fn in calls:
+            fn()
+
     for _ in range(args.warmup):
-        store()
-        decode()
+        step()
     torch.cuda.synchronize(dev)
+    run = step
+    if args.graph:
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize(dev)
+        run = graph.replay
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize(dev)
 
     # whole-step timing: K steps back to back between two events
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     start.record()
     for _ in range(args.steps):
-        store()
-        decode()
+        run()
     end.record()
     torch.cuda.synchronize(dev)
     ms_step = start.elapsed_time(end) / args.steps
 
     # per-call durations: events around each call, on the launch stream
     n = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(n)]
     torch.cuda.synchronize(dev)
     for i in range(n):
         ev[i][0].record()
-        store()
-        ev[i][1].record()
-        decode()
-        ev[i][2].record()
+        for j, (_, fn) in enumerate(calls):
+            fn()
+            ev[i][j + 1].record()
     torch.cuda.synchronize(dev)
-    ms_store = sum(e[0].elapsed_time(e[1]) for e in ev) / n
-    ms_decode = sum(e[1].elapsed_time(e[2]) for e in ev) / n
+    ms_call = {name: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / n
+               for j, (name, _) in enumerate(calls)}
 
     db = decode_bytes(case)
     sb = store_bytes(case.batch, case.num_kv_heads, case.head_dim)
     gbs = (db + sb) / (ms_step * 1e-3) / 1e9
-    dec_gbs = db / (ms_decode * 1e-3) / 1e9
-    traffic = traffic_from_profile(DECODE_SRC)
+    if args.mode == "fused":
+        dom, dom_bytes = "pa_decode_step", db + sb
+        dom_desc = "pa_decode_step (store + split-K decode + merge)"
+    else:
+        dom, dom_bytes = "pa_decode", db
+        dom_desc = "pa_decode (split-K + merge)"
+    dom_gbs = dom_bytes / (ms_call[dom] * 1e-3) / 1e9
+    traffic = traffic_from_profile(DECODE_SRC, args.mode)
 
     rec = {
         "metric": "paged decode: KV GB/s (% HBM peak) + tokens/s at Qwen3-8B shape, batch 256",
@@ -276,17 +315,17 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": W.DESCRIPTIONS[args.config] + "; step = store of the batch's "
                    "new tokens + decode, one layer", "global_batch": case.batch,
-                   "seq_len": max_ctx, "parallelism": "none (1 GPU)"},
+                   "seq_len": max_ctx, "parallelism": "none (1 GPU)",
+                   "step_mode": args.mode + (" + hip graph" if args.graph else "")},
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": {"per_layer": round(case.batch / (ms_step * 1e-3), 1),
                          "model_36_layers": round(case.batch / (LAYERS_QWEN3_8B * ms_step * 1e-3),
                                                   1)},
-        "ms_store": round(ms_store, 5),
-        "ms_decode": round(ms_decode, 5),
+        "ms_per_call": {k: round(v, 5) for k, v in ms_call.items()},
         "algorithmic_bytes": {"decode": db, "store": sb},
-        "roofline": {"bound": "hbm", "kernel": "pa_decode (split-K + merge)",
-                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "roofline": {"bound": "hbm", "kernel": dom_desc,
+                     "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
     if args.prefill:
         rec["prefill"] = run_prefill(args, torch, B, W, dev)

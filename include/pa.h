@@ -141,6 +141,34 @@ size_t pa_decode_workspace_size_ex(const pa_desc* desc, int32_t num_seqs,
                                    int32_t max_context_len, int32_t partition_blocks);
 
 /*
+ * pa_decode_step -- one decode step in one pass: pa_store_kv of each
+ * sequence's newest token followed by pa_decode, fused ([P1 §12.6] Attention
+ * forward stores K/V, then runs decode attention; [P1 §12.7] runs the
+ * per-layer step as a replayed CUDA graph with slot -1 / length 0 padding).
+ *
+ * For every sequence b with n = context_lens[b] > 0: the newest token
+ * (position n-1) is k_new[b], v_new[b]; they are written to cache row
+ * slot_mapping[b] (skipped if -1 or out of range) and attended to from the
+ * inputs directly, so no kernel of the call reads that row back. Tokens
+ * 0 .. n-2 are read from the cache through block_tables. The output is the
+ * pa_decode output of the stored cache (up to fp32 summation order). Rows
+ * with n == 0 get zeros and store nothing.
+ *
+ *   q, block_tables, context_lens, max_context_len, scale, out, workspace:
+ *                 as pa_decode (same workspace size).
+ *   k_new, v_new  device, bf16 [num_seqs, H_kv, d], row strides in elements
+ *                 (multiples of 8, >= H_kv*d), 16-byte aligned.
+ *   k_cache, v_cache  device, written (one row per sequence) and read.
+ *   slot_mapping  device, int32 [num_seqs].
+ */
+int pa_decode_step(const void* q, const void* k_new, int64_t k_row_stride, const void* v_new,
+                   int64_t v_row_stride, void* k_cache, void* v_cache,
+                   const int32_t* slot_mapping, const int32_t* block_tables,
+                   int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                   int32_t max_context_len, float scale, void* out, void* workspace,
+                   size_t workspace_bytes, const pa_desc* desc, void* stream);
+
+/*
  * pa_prefill_varlen -- causal attention of a packed batch of new tokens over
  * paged K/V. [P1 §12.6] prefill branch with prefix cache
  * (flash_attn_varlen_func with a block table; the cu_seqlens notes).

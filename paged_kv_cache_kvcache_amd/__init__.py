@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     load,
     pa_build_metadata,
     pa_decode,
+    pa_decode_step,
     pa_decode_workspace_size,
     pa_prefill_varlen,
     pa_store_kv,

@@ -25,6 +25,7 @@ PA_ERR_HIP = -4
 # Every symbol include/pa.h declares (checked by the CPU test suite).
 EXPORTS = (
     "pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_partitioned",
+    "pa_decode_step",
     "pa_decode_workspace_size_ex", "pa_prefill_varlen", "pa_build_metadata",
     "pa_last_error", "pa_version",
 )
@@ -77,6 +78,9 @@ def load():
     lib.pa_decode_partitioned.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, f32, vp, vp, sz, i32,
                                           pdesc, vp]
     lib.pa_decode_partitioned.restype = ctypes.c_int
+    lib.pa_decode_step.argtypes = [vp, vp, i64, vp, i64, vp, vp, vp, vp, i32, vp, i32, i32, f32, vp,
+                                   vp, sz, pdesc, vp]
+    lib.pa_decode_step.restype = ctypes.c_int
     lib.pa_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, f32, vp, pdesc,
                                       vp]
     lib.pa_prefill_varlen.restype = ctypes.c_int
@@ -195,6 +199,48 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
                                      batch, int(max_context_len), float(scale), out.data_ptr(),
                                      ws_ptr, ws_bytes, int(partition_blocks), ctypes.byref(desc),
                                      _stream(q)))
+
+
+def pa_decode_step(q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens,
+                   scale: float, out, max_context_len: int | None = None, workspace=None) -> None:
+    """Fused store of each sequence's newest token (``k_new``/``v_new``
+    ``[batch, H_kv, d]``, row-strided views allowed) + paged decode."""
+    import torch
+    _need_cuda(q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens, out)
+    _check_cache_pair(k_cache, v_cache)
+    for t in (q, k_new, v_new, out):
+        if t.dtype != torch.bfloat16:
+            raise ValueError("q, k_new, v_new and out must be bf16")
+    for t in (slot_mapping, block_tables, context_lens):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("slot_mapping, block_tables and context_lens must be contiguous int32")
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous")
+    batch, h_q, d = q.shape
+    h_kv = k_cache.shape[2]
+    for t in (k_new, v_new):
+        if t.dim() != 3 or tuple(t.shape) != (batch, h_kv, d) or t.stride(2) != 1 \
+                or t.stride(1) != d:
+            raise ValueError("k_new/v_new must be [batch, H_kv, d] with contiguous heads")
+    if tuple(out.shape) != (batch, h_q, d) or slot_mapping.numel() != batch:
+        raise ValueError("out must match q; slot_mapping must be [batch]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != batch or context_lens.numel() != batch:
+        raise ValueError("block_tables must be [batch, max_blocks], context_lens [batch]")
+    max_blocks = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = max_blocks * int(k_cache.shape[1])
+    desc = _desc_from_cache(k_cache, h_q)
+    lib = load()
+    need = int(lib.pa_decode_workspace_size(ctypes.byref(desc), batch, int(max_context_len)))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_decode_step(q.data_ptr(), k_new.data_ptr(), k_new.stride(0), v_new.data_ptr(),
+                              v_new.stride(0), k_cache.data_ptr(), v_cache.data_ptr(),
+                              slot_mapping.data_ptr(), block_tables.data_ptr(), max_blocks,
+                              context_lens.data_ptr(), batch, int(max_context_len), float(scale),
+                              out.data_ptr(), ws_ptr, ws_bytes, ctypes.byref(desc), _stream(q)))
 
 
 def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,

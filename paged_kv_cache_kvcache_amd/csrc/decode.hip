@@ -45,6 +45,15 @@ struct DecodeArgs {
   float* ws_o;   // [num_seqs, H_q, max_parts, d] fp32 unnormalised partial outputs
   float* ws_ml;  // [num_seqs, H_q, max_parts, 2]  (running max in log2 units, sum)
   uint16_t* out;
+  // fused store (pa_decode_step): the newest token of each sequence comes
+  // from k_new/v_new and is written to the cache at slot_mapping[b]
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_cache_w;  // the caches, written only by the fused store
+  uint16_t* v_cache_w;
+  const int32_t* slot_mapping;
+  int64_t k_new_stride;  // elements between tokens of k_new / v_new
+  int64_t v_new_stride;
   int64_t num_blocks;
   int32_t max_blocks;
   int32_t num_seqs;
@@ -80,9 +89,6 @@ __device__ __forceinline__ int clamp_len(int n, int max_blocks) {
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 2
 #endif
-#ifndef PA_DECODE_PIPE
-#define PA_DECODE_PIPE 0
-#endif
 
 // K/V rows are read exactly once per call: nontemporal loads keep them from
 // displacing reusable lines (tables, q) in the caches.
@@ -96,16 +102,41 @@ __device__ __forceinline__ uint4 load16(const char* p) {
 #endif
 }
 
+#ifndef PA_DECODE_PV_BF16
+#define PA_DECODE_PV_BF16 1
+#endif
+#ifndef PA_DECODE_PIPE
+#define PA_DECODE_PIPE 1
+#endif
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+// Two fp32 -> packed bf16 (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t pack2_bf16_hw(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
 // Raw v_exp_f32 (2^x). Arguments are <= 0 here; results below the normal
 // range flush to zero, which is what a softmax weight that small should be.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lane geometry: d/8 lanes hold one token's head vector (16 bytes each), so a
+// wave load instruction covers TPI tokens.
+template <int D>
+struct Lanes {
+  static constexpr int LPT = D / 8;        // lanes per token vector
+  static constexpr int TPI = kWave / LPT;  // tokens per wave load instruction
+};
+
 // Per-wave state of one work item.
-template <int D, int G, int U>
+template <int D, int G>
 struct SplitState {
-  static constexpr int LPT = D / 8;            // lanes per token vector
-  static constexpr int TPI = kWave / LPT;      // tokens per wave load instruction
-  static constexpr int CHUNK = TPI * U;        // tokens per chunk
   uint32_t qv[G][4];
   float m[G], l[G], acc[G][8];  // running max (log2 units), sum, unnormalised output
 };
@@ -114,11 +145,11 @@ struct SplitState {
 // wave-uniform base plus one per-lane offset; the tail chunk clamps every
 // token index to the last valid one (masked later), so no address ever
 // leaves the sequence's blocks.
-template <int D, int G, int U, bool TAIL>
+template <int D, int U, bool TAIL>
 __device__ __forceinline__ void issue_chunk(const char* kbase, const char* vbase, int64_t row_bytes,
                                             int lane_off, int row, int last, uint4 (&kr)[U],
                                             uint4 (&vr)[U]) {
-  using S = SplitState<D, G, U>;
+  using S = Lanes<D>;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if constexpr (TAIL) {
@@ -139,57 +170,11 @@ __device__ __forceinline__ void issue_chunk(const char* kbase, const char* vbase
   }
 }
 
-#ifndef PA_DECODE_LAZY
-#define PA_DECODE_LAZY 0
-#endif
-// Lazy rescaling: a row's reference max m is raised only when a score
-// exceeds it by more than 2^kLazyLog2, so weights 2^(s-m) stay <= 256 and the
-// accumulator rescale (G*8 multiplies + exps) runs only on those rare tokens.
-// The result is the same softmax: numerator and denominator share m.
-constexpr float kLazyLog2 = 8.f;
-
 template <int D, int G, int U, bool TAIL>
-__device__ __forceinline__ void compute_chunk(SplitState<D, G, U>& st, float scale_log2, int row,
+__device__ __forceinline__ void compute_chunk(SplitState<D, G>& st, float scale_log2, int row,
                                               int nvalid, const uint4 (&kr)[U],
                                               const uint4 (&vr)[U]) {
-  using S = SplitState<D, G, U>;
-#if PA_DECODE_LAZY
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const bool valid = !TAIL || (u * S::TPI + row < nvalid);
-    float sc[G];
-    float over = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      sc[h] = group_sum<S::LPT>(dot8_bf16(kr[u], st.qv[h], 0.f)) * scale_log2;
-      over = fmaxf(over, sc[h] - st.m[h]);  // +inf before the row's first token
-    }
-    if (valid && over > kLazyLog2) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float mnew = fmaxf(st.m[h], sc[h]);
-        const float alpha = fast_exp2(st.m[h] - mnew);  // 0 on the first token
-        st.l[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) st.acc[h][e] *= alpha;
-        st.m[h] = mnew;
-      }
-    }
-    float vf[8];
-    vf[0] = bf16_lo(vr[u].x); vf[1] = bf16_hi(vr[u].x);
-    vf[2] = bf16_lo(vr[u].y); vf[3] = bf16_hi(vr[u].y);
-    vf[4] = bf16_lo(vr[u].z); vf[5] = bf16_hi(vr[u].z);
-    vf[6] = bf16_lo(vr[u].w); vf[7] = bf16_hi(vr[u].w);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float p = fast_exp2(sc[h] - st.m[h]);
-      if constexpr (TAIL) p = valid ? p : 0.f;
-      st.l[h] += p;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st.acc[h][e] = fmaf(p, vf[e], st.acc[h][e]);
-    }
-  }
-#else
+  using S = Lanes<D>;
   float s[U][G];  // raw q.k (unscaled)
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -218,6 +203,34 @@ __device__ __forceinline__ void compute_chunk(SplitState<D, G, U>& st, float sca
     st.m[h] = mnew;
     negm[h] = -msafe;
   }
+  if constexpr (PA_DECODE_PV_BF16 && U % 2 == 0) {
+  // P.V on token pairs with v_dot2_f32_bf16: (V[t][e], V[t+1][e]) packed by
+  // v_perm, weights rounded to bf16 as the MFMA prefill does. The sum l adds
+  // the same rounded weights, so the output stays an exact weighted mean.
+#pragma unroll
+  for (int u = 0; u < U; u += 2) {
+    uint32_t ppair[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float p0 = fast_exp2(fmaf(s[u][h], scale_log2, negm[h]));
+      const float p1 = fast_exp2(fmaf(s[u + 1][h], scale_log2, negm[h]));
+      ppair[h] = pack2_bf16_hw(p0, p1);
+      st.l[h] += bf16_lo(ppair[h]) + bf16_hi(ppair[h]);
+    }
+    const uint32_t a[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+    const uint32_t c[4] = {vr[u + 1].x, vr[u + 1].y, vr[u + 1].z, vr[u + 1].w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = __builtin_amdgcn_perm(c[w], a[w], 0x05040100u);  // element 2w
+      const uint32_t hi = __builtin_amdgcn_perm(c[w], a[w], 0x07060302u);  // element 2w+1
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        st.acc[h][2 * w] = dot2_bf16(lo, ppair[h], st.acc[h][2 * w]);
+        st.acc[h][2 * w + 1] = dot2_bf16(hi, ppair[h], st.acc[h][2 * w + 1]);
+      }
+    }
+  }
+  } else {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     float vf[8];
@@ -233,42 +246,28 @@ __device__ __forceinline__ void compute_chunk(SplitState<D, G, U>& st, float sca
       for (int e = 0; e < 8; ++e) st.acc[h][e] = fmaf(p, vf[e], st.acc[h][e]);
     }
   }
-#endif
+  }
 }
 
-template <int D, int G>
+template <int D, int G, bool FUSED>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
 void decode_split_kernel(DecodeArgs a) {
   constexpr int U = PA_DECODE_UNROLL;
-  using S = SplitState<D, G, U>;
-  constexpr int LPT = S::LPT;
-  constexpr int CHUNK = S::CHUNK;
+  using S = SplitState<D, G>;
+  constexpr int LPT = Lanes<D>::LPT;
+  constexpr int CHUNK = Lanes<D>::TPI * U;  // tokens per chunk
   static_assert(kBlockSize % CHUNK == 0, "a chunk never straddles a block");
 
   const int H_kv = a.num_kv_heads;
   const int H_q = H_kv * G;
-#ifndef PA_DECODE_ORDER
-#define PA_DECODE_ORDER 1
-#endif
+  // Items are dispatched highest partition first: the grid then drains on the
+  // first partitions, which every sequence has, instead of on the tails of
+  // a few long sequences.
   int idx = blockIdx.x;
-#if PA_DECODE_ORDER == 2
-  // partition fastest: a sequence's items are dispatched together
-  const int part = idx % a.max_parts;
-  idx /= a.max_parts;
-  const int g = idx % H_kv;
-  const int b = idx / H_kv;
-#else
   const int g = idx % H_kv;
   idx /= H_kv;
   const int b = idx % a.num_seqs;
-#if PA_DECODE_ORDER == 1
-  // highest partitions first: the items dispatched last are the first
-  // partitions, which every sequence has, so the grid drains evenly
   const int part = a.max_parts - 1 - idx / a.num_seqs;
-#else
-  const int part = idx / a.num_seqs;
-#endif
-#endif
   const int lane = threadIdx.x;
   const int sub = lane % LPT;  // which 8 elements of the head vector
   const int row = lane / LPT;  // which token of a load instruction
@@ -306,53 +305,73 @@ void decode_split_kernel(DecodeArgs a) {
   const int tail_lane_off = (g * D + sub * 8) * 2;
   const char* kc = reinterpret_cast<const char*>(a.k_cache);
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
-  const int nfull = (end - start) / CHUNK;  // chunks with no token past the end
-  // base byte offset of full chunk i; a broken table entry reads block 0 and
-  // the chunk is skipped
-  auto chunk_off = [&](int i, bool& ok) -> int64_t {
+  // With the fused store the newest token (position n-1) is taken from
+  // k_new/v_new instead of the cache; only [start, cend) is read from the cache.
+  const int cend = (FUSED && end == n) ? n - 1 : end;
+  const int nfull = (cend - start) / CHUNK;  // chunks with no token past cend
+  // Byte offset of full chunk i. A broken table entry (precondition
+  // violated) is read as block 0: the result is then meaningless but every
+  // access stays inside the pool.
+  auto chunk_off = [&](int i) -> int64_t {
     const int cc = start + i * CHUNK;
-    const int blk = bt[cc / kBlockSize];
-    ok = blk >= 0 && blk < a.num_blocks;
-    return ((int64_t)(ok ? blk : 0) * kBlockSize + (cc % kBlockSize)) * row_bytes;
+    int blk = bt[cc / kBlockSize];
+    blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+    return ((int64_t)blk * kBlockSize + (cc % kBlockSize)) * row_bytes;
   };
 #if PA_DECODE_PIPE
-  // Two register buffers: chunk i+1's loads are in flight while chunk i is
-  // computed. The prefetch index is clamped to the last full chunk, so every
-  // issue is unconditional and the memory-counter waits are static.
+  // Software pipeline over two register buffers: chunk i+1's loads are in
+  // flight while chunk i is multiplied. The loop body has no branches and the
+  // prefetch index is clamped, so the same number of loads is outstanding on
+  // every path and the compiler's memory-counter waits stay partial.
   if (nfull > 0) {
     uint4 ka[U], va[U], kb[U], vb[U];
-    bool oka, okb;
-    int64_t off = chunk_off(0, oka);
-    issue_chunk<D, G, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, ka, va);
-    for (int i = 0; i < nfull; i += 2) {
-      off = chunk_off(min(i + 1, nfull - 1), okb);
-      issue_chunk<D, G, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, kb, vb);
-      if (oka) compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
-      if (i + 1 >= nfull) break;
-      off = chunk_off(min(i + 2, nfull - 1), oka);
-      issue_chunk<D, G, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, ka, va);
-      if (okb) compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
+    int64_t off = chunk_off(0);
+    issue_chunk<D, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, ka, va);
+    int i = 0;
+    for (; i + 2 <= nfull; i += 2) {
+      off = chunk_off(i + 1);
+      issue_chunk<D, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, kb, vb);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the multiply
+      compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
+      off = chunk_off(min(i + 2, nfull - 1));
+      issue_chunk<D, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, ka, va);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
     }
+    if (i < nfull) compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
   }
 #else
   for (int i = 0; i < nfull; ++i) {
-    bool ok;
-    const int64_t off = chunk_off(i, ok);
-    if (!ok) continue;
+    const int64_t off = chunk_off(i);
     uint4 kr[U], vr[U];
-    issue_chunk<D, G, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, kr, vr);
+    issue_chunk<D, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, kr, vr);
     compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, kr, vr);
   }
 #endif
   const int c = start + nfull * CHUNK;
-  if (c < end) {
+  if (c < cend) {
     const int blk = bt[c / kBlockSize];
     if (blk >= 0 && blk < a.num_blocks) {
       const int64_t off = ((int64_t)blk * kBlockSize + (c % kBlockSize)) * row_bytes;
       uint4 kr[U], vr[U];
-      issue_chunk<D, G, U, true>(kc + off, vc + off, row_bytes, tail_lane_off, row, end - 1 - c,
+      issue_chunk<D, U, true>(kc + off, vc + off, row_bytes, tail_lane_off, row, cend - 1 - c,
                                  kr, vr);
-      compute_chunk<D, G, U, true>(st, a.scale_log2, row, end - c, kr, vr);
+      compute_chunk<D, G, U, true>(st, a.scale_log2, row, cend - c, kr, vr);
+    }
+  }
+  if (FUSED && end == n) {
+    // the newest token: attend to it from registers and write it to its slot
+    // (no work item of this call reads that cache row)
+    const uint4 kt = *reinterpret_cast<const uint4*>(a.k_new + (int64_t)b * a.k_new_stride + g * D + sub * 8);
+    const uint4 vt = *reinterpret_cast<const uint4*>(a.v_new + (int64_t)b * a.v_new_stride + g * D + sub * 8);
+    const uint4 kr1[1] = {kt};
+    const uint4 vr1[1] = {vt};
+    compute_chunk<D, G, 1, true>(st, a.scale_log2, row, 1, kr1, vr1);
+    const int slot = a.slot_mapping[b];
+    if (row == 0 && slot >= 0 && slot < a.num_blocks * kBlockSize) {
+      const int64_t dst = (int64_t)slot * H_kv * D + g * D + sub * 8;
+      *reinterpret_cast<uint4*>(a.k_cache_w + dst) = kt;
+      *reinterpret_cast<uint4*>(a.v_cache_w + dst) = vt;
     }
   }
 
@@ -441,18 +460,34 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a, int 
 
 using SplitFn = void (*)(DecodeArgs);
 
-template <int D>
+template <int D, bool FUSED>
 SplitFn pick_split(int G) {
   switch (G) {
-    case 1: return decode_split_kernel<D, 1>;
-    case 2: return decode_split_kernel<D, 2>;
-    case 4: return decode_split_kernel<D, 4>;
-    case 8: return decode_split_kernel<D, 8>;
+    case 1: return decode_split_kernel<D, 1, FUSED>;
+    case 2: return decode_split_kernel<D, 2, FUSED>;
+    case 4: return decode_split_kernel<D, 4, FUSED>;
+    case 8: return decode_split_kernel<D, 8, FUSED>;
   }
   return nullptr;
 }
 
-int default_partition_blocks(const pa_desc*, int32_t, int32_t) { return 4; }
+// Resident work items the split kernel keeps on an MI355X: 256 CUs x 8 waves.
+// A fixed constant (not a device query) so the workspace size is a pure
+// function of the arguments.
+constexpr int64_t kResidentItems = 256 * 8;
+
+// Longest partition (8, 4, 2 or 1 blocks) whose item count still fills half
+// the resident slots, estimating the mean context as max_context_len / 2.
+// Long partitions amortise each item's set-up and keep its loads streaming;
+// short ones keep small batches spread over the whole chip.
+int default_partition_blocks(const pa_desc* d, int32_t num_seqs, int32_t max_ctx) {
+  const int64_t mean_ctx = max(1, max_ctx / 2);
+  for (int p = 8; p > 1; p >>= 1) {
+    const int64_t per_seq = (mean_ctx + (int64_t)p * kBlockSize - 1) / ((int64_t)p * kBlockSize);
+    if ((int64_t)num_seqs * d->num_kv_heads * per_seq >= kResidentItems / 2) return p;
+  }
+  return 1;
+}
 
 struct Plan {
   int part_tokens;
@@ -469,6 +504,99 @@ Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part
                                 : (size_t)num_seqs * d->num_q_heads * p.max_parts *
                                       (size_t)(d->head_dim + 2) * sizeof(float);
   return p;
+}
+
+struct NewTokens {  // the fused store's inputs (all null for plain decode)
+  const void* k;
+  int64_t k_stride;
+  const void* v;
+  int64_t v_stride;
+  const int32_t* slot_mapping;
+};
+
+int launch_decode(const char* who, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                  float scale, void* out, void* workspace, size_t workspace_bytes,
+                  int32_t partition_blocks, const pa_desc* desc, void* stream,
+                  const NewTokens* nt) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || partition_blocks < 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: negative size", who);
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if ((int64_t)max_blocks_per_seq * kBlockSize < max_context_len)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_context_len %d exceeds %d table entries", who,
+                max_context_len, max_blocks_per_seq);
+  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15u)
+    return fail(PA_ERR_INVALID_ARG, "%s: q, caches and out must be 16-byte aligned", who);
+  const int G = desc->num_q_heads / desc->num_kv_heads;
+  const int D = desc->head_dim;
+  const int row = desc->num_kv_heads * D;
+  if (nt) {
+    if (!nt->k || !nt->v || !nt->slot_mapping)
+      return fail(PA_ERR_INVALID_ARG, "%s: NULL new-token pointer", who);
+    if (nt->k_stride < row || nt->v_stride < row || (nt->k_stride % 8) || (nt->v_stride % 8) ||
+        (((uintptr_t)nt->k | (uintptr_t)nt->v) & 15u))
+      return fail(PA_ERR_INVALID_ARG,
+                  "%s: k_new/v_new need 16-byte aligned rows with stride >= H_kv*d", who);
+  }
+  const Plan plan = make_plan(desc, num_seqs, max_context_len, partition_blocks);
+  if (plan.ws_bytes) {
+    if (!workspace || workspace_bytes < plan.ws_bytes)
+      return fail(PA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", who,
+                  workspace ? workspace_bytes : (size_t)0, plan.ws_bytes);
+    if ((uintptr_t)workspace & 15u)
+      return fail(PA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", who);
+  }
+  const int64_t items = (int64_t)num_seqs * desc->num_kv_heads * plan.max_parts;
+  if (items > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "%s: grid too large", who);
+
+  DecodeArgs a;
+  a.q = (const uint16_t*)q;
+  a.k_cache = (const uint16_t*)k_cache;
+  a.v_cache = (const uint16_t*)v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  const size_t o_floats = (size_t)num_seqs * desc->num_q_heads * plan.max_parts * D;
+  a.ws_o = plan.ws_bytes ? (float*)workspace : nullptr;
+  a.ws_ml = plan.ws_bytes ? (float*)workspace + o_floats : nullptr;
+  a.out = (uint16_t*)out;
+  a.k_new = nt ? (const uint16_t*)nt->k : nullptr;
+  a.v_new = nt ? (const uint16_t*)nt->v : nullptr;
+  a.k_cache_w = nt ? (uint16_t*)k_cache : nullptr;
+  a.v_cache_w = nt ? (uint16_t*)v_cache : nullptr;
+  a.slot_mapping = nt ? nt->slot_mapping : nullptr;
+  a.k_new_stride = nt ? nt->k_stride : 0;
+  a.v_new_stride = nt ? nt->v_stride : 0;
+  a.num_blocks = desc->num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.part_tokens = plan.part_tokens;
+  a.max_parts = plan.max_parts;
+  a.scale_log2 = scale * kLog2e;
+
+  hipStream_t s = (hipStream_t)stream;
+  SplitFn split = nt ? (D == 128 ? pick_split<128, true>(G) : pick_split<64, true>(G))
+                     : (D == 128 ? pick_split<128, false>(G) : pick_split<64, false>(G));
+  hipLaunchKernelGGL(split, dim3((unsigned)items), dim3(kWave), 0, s, a);
+  rc = launch_status(who);
+  if (rc) return rc;
+  if (plan.max_parts > 1) {
+    const unsigned rows = (unsigned)num_seqs * desc->num_q_heads;
+    if (D == 128)
+      hipLaunchKernelGGL(decode_reduce_kernel<128>, dim3(rows), dim3(kWave), 0, s, a,
+                         desc->num_q_heads);
+    else
+      hipLaunchKernelGGL(decode_reduce_kernel<64>, dim3(rows), dim3(kWave), 0, s, a,
+                         desc->num_q_heads);
+    rc = launch_status(who);
+    if (rc) return rc;
+  }
+  return PA_OK;
 }
 
 }  // namespace
@@ -494,67 +622,9 @@ extern "C" int pa_decode_partitioned(const void* q, const void* k_cache, const v
                                      void* workspace, size_t workspace_bytes,
                                      int32_t partition_blocks, const pa_desc* desc,
                                      void* stream) {
-  using namespace pa;
-  int rc = check_desc(desc);
-  if (rc) return rc;
-  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || partition_blocks < 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: negative size");
-  if (num_seqs == 0) return PA_OK;
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: NULL pointer");
-  if ((int64_t)max_blocks_per_seq * kBlockSize < max_context_len)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: max_context_len %d exceeds %d table entries",
-                max_context_len, max_blocks_per_seq);
-  if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15u)
-    return fail(PA_ERR_INVALID_ARG, "pa_decode: q, caches and out must be 16-byte aligned");
-  const Plan plan = make_plan(desc, num_seqs, max_context_len, partition_blocks);
-  if (plan.ws_bytes) {
-    if (!workspace || workspace_bytes < plan.ws_bytes)
-      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace %zu bytes < %zu needed",
-                  workspace ? workspace_bytes : (size_t)0, plan.ws_bytes);
-    if ((uintptr_t)workspace & 15u)
-      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace must be 16-byte aligned");
-  }
-  const int G = desc->num_q_heads / desc->num_kv_heads;
-  const int D = desc->head_dim;
-  const int64_t items = (int64_t)num_seqs * desc->num_kv_heads * plan.max_parts;
-  if (items > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "pa_decode: grid too large");
-
-  DecodeArgs a;
-  a.q = (const uint16_t*)q;
-  a.k_cache = (const uint16_t*)k_cache;
-  a.v_cache = (const uint16_t*)v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  const size_t o_floats = (size_t)num_seqs * desc->num_q_heads * plan.max_parts * D;
-  a.ws_o = plan.ws_bytes ? (float*)workspace : nullptr;
-  a.ws_ml = plan.ws_bytes ? (float*)workspace + o_floats : nullptr;
-  a.out = (uint16_t*)out;
-  a.num_blocks = desc->num_blocks;
-  a.max_blocks = max_blocks_per_seq;
-  a.num_seqs = num_seqs;
-  a.num_kv_heads = desc->num_kv_heads;
-  a.part_tokens = plan.part_tokens;
-  a.max_parts = plan.max_parts;
-  a.scale_log2 = scale * kLog2e;
-
-  hipStream_t s = (hipStream_t)stream;
-  SplitFn split = D == 128 ? pick_split<128>(G) : pick_split<64>(G);
-  hipLaunchKernelGGL(split, dim3((unsigned)items), dim3(kWave), 0, s, a);
-  rc = launch_status("pa_decode split");
-  if (rc) return rc;
-  if (plan.max_parts > 1) {
-    const unsigned rows = (unsigned)num_seqs * desc->num_q_heads;
-    if (D == 128)
-      hipLaunchKernelGGL(decode_reduce_kernel<128>, dim3(rows), dim3(kWave), 0, s, a,
-                         desc->num_q_heads);
-    else
-      hipLaunchKernelGGL(decode_reduce_kernel<64>, dim3(rows), dim3(kWave), 0, s, a,
-                         desc->num_q_heads);
-    rc = launch_status("pa_decode reduce");
-    if (rc) return rc;
-  }
-  return PA_OK;
+  return pa::launch_decode("pa_decode", q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                           context_lens, num_seqs, max_context_len, scale, out, workspace,
+                           workspace_bytes, partition_blocks, desc, stream, nullptr);
 }
 
 extern "C" int pa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -565,4 +635,17 @@ extern "C" int pa_decode(const void* q, const void* k_cache, const void* v_cache
   return pa_decode_partitioned(q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                                context_lens, num_seqs, max_context_len, scale, out, workspace,
                                workspace_bytes, 0, desc, stream);
+}
+
+extern "C" int pa_decode_step(const void* q, const void* k_new, int64_t k_row_stride,
+                              const void* v_new, int64_t v_row_stride, void* k_cache,
+                              void* v_cache, const int32_t* slot_mapping,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_context_len, float scale, void* out, void* workspace,
+                              size_t workspace_bytes, const pa_desc* desc, void* stream) {
+  const pa::NewTokens nt{k_new, k_row_stride, v_new, v_row_stride, slot_mapping};
+  return pa::launch_decode("pa_decode_step", q, k_cache, v_cache, block_tables,
+                           max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale,
+                           out, workspace, workspace_bytes, 0, desc, stream, &nt);
 }

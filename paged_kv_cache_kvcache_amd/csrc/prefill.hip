@@ -20,7 +20,8 @@
 //     transposed (d-major) in LDS in that key order.
 //   * Online softmax per query column: base-2 exponent with scale*log2(e)
 //     folded in, running max exchanged across the 4 lane groups of a column,
-//     P rounded to bf16 for the MFMA, fp32 accumulation, bf16 output.
+//     P rounded to bf16 for the MFMA (the row sum adds the same rounded
+//     weights), fp32 accumulation, bf16 output.
 //   * Keys are staged 64 at a time (a stage never straddles a 256-token block,
 //     so one block-table lookup per stage), double-buffered in LDS with
 //     register staging two stages ahead of the multiply.
@@ -313,15 +314,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
           const float msafe = (m[j] == -INFINITY) ? 0.f : m[j];
           float p[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], a.scale_log2, -msafe));
-            l[j] += p[i];
-          }
+          for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], a.scale_log2, -msafe));
           uint4 pk;
           pk.x = pack2_bf16(p[0], p[1]);
           pk.y = pack2_bf16(p[2], p[3]);
           pk.z = pack2_bf16(p[4], p[5]);
           pk.w = pack2_bf16(p[6], p[7]);
+          // the sum adds the rounded weights the MFMA sees: an exact weighted mean
+          l[j] += (bf16_lo(pk.x) + bf16_hi(pk.x)) + (bf16_lo(pk.y) + bf16_hi(pk.y)) +
+                  (bf16_lo(pk.z) + bf16_hi(pk.z)) + (bf16_lo(pk.w) + bf16_hi(pk.w));
           pf[j] = __builtin_bit_cast(bf16x8, pk);
         }
         // ---- O^T += V^T P^T
