@@ -73,6 +73,7 @@ struct PrefillArgs {
   int32_t max_blocks;
   int32_t num_seqs;
   int32_t num_kv_heads;
+  int32_t max_rblocks;  // position blocks of the longest sequence
   float scale_log2;
 };
 
@@ -178,11 +179,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
   const int H_kv = a.num_kv_heads;
   const int H_q = H_kv * G;
+#ifndef PA_PREFILL_ORDER
+#define PA_PREFILL_ORDER 1
+#endif
   int idx = blockIdx.x;
   const int g = idx % H_kv;
   idx /= H_kv;
+#if PA_PREFILL_ORDER == 1
+  // A sequence's position blocks are consecutive (last positions first) and
+  // kv-head is fastest, so the blocks of one (sequence, kv-head), which read
+  // the same K/V, run together on one XCD and share its L2.
+  const int r = idx % a.max_rblocks;  // position block counted from the end
+  const int b = idx / a.max_rblocks;
+#else
   const int b = idx % a.num_seqs;
   const int r = idx / a.num_seqs;  // position block counted from the end
+#endif
 
   const int q0 = a.cu_q[b];
   const int q_len = a.cu_q[b + 1] - q0;
@@ -420,6 +432,7 @@ extern "C" int pa_prefill_varlen(const void* q, const void* k_cache, const void*
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_kv_heads = desc->num_kv_heads;
+  a.max_rblocks = (max_seqlen_q + QB - 1) / QB;
   a.scale_log2 = scale * kLog2e;
   PrefillFn fn = D == 128 ? pick<128>(G) : pick<64>(G);
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a);
