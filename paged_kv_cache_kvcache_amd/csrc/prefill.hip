@@ -26,8 +26,8 @@
 //     so one block-table lookup per stage), double-buffered in LDS with
 //     register staging two stages ahead of the multiply.
 //   * Causal work skipping: stages past the work item's last query are never
-//     loaded; a wave skips the 32-key steps that lie after all its queries;
-//     only steps that cross the diagonal apply the mask.
+//     loaded; a wave skips the stages that lie after all its queries; only
+//     stages that cross the diagonal apply the mask.
 //   * Grid order: per sequence the last position blocks (the most keys) come
 //     first; consecutive workgroups differ in kv-head so one (sequence,
 //     kv-head)'s blocks, which re-read the same K/V, land on the same XCD.
@@ -99,6 +99,14 @@ template <> struct VVec<16> { typedef __attribute__((ext_vector_type(8))) unsign
 // it: lane group j holds keys 4j..4j+3 (first 16-key tile) then 16+4j..16+4j+3.
 __device__ __forceinline__ int key_slot(int k) {
   return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
+}
+
+// acc + lo + hi of a packed bf16 pair, exactly in fp32 (v_dot2_f32_bf16 with
+// the pair (1.0, 1.0)).
+__device__ __forceinline__ float sum_pair_bf16(uint32_t pair, float acc) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                         __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
 }
 
 // Two fp32 -> packed bf16 (v_cvt_pk_bf16_f32, round to nearest even).
@@ -264,89 +272,97 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
                         const typename VVec<GG::VW>::T (&vready)[2], u32x4 (&knext)[GG::KCHUNKS],
                         typename VVec<GG::VW>::T (&vnext)[2]) {
     load_stage<D>(a, bt, g, kmax, min(st + 2, n_stages - 1), knext, vnext);
-      const char* ks_lds = lds + (st & 1) * GG::STAGE;
-      const char* vt_lds = ks_lds + GG::KBYTES;
-
+    const char* ks_lds = lds + (st & 1) * GG::STAGE;
+    const char* vt_lds = ks_lds + GG::KBYTES;
+    const int key0 = st * kKT;  // absolute position of the stage's first key
+    if (key0 <= off + wmax) {   // else every key is after every query of the wave
+      // ---- S^T = K Q^T for the stage's 64 keys x (kNT x 16) columns
+      f32x4 s[kKT / 16][kNT];
 #pragma unroll
-      for (int sub = 0; sub < kKT / 32; ++sub) {
-        const int key0 = st * kKT + sub * 32;  // absolute position of the step's first key
-        if (key0 > off + wmax) continue;       // every key is after every query of the wave
-        // ---- S^T = K Q^T for 32 keys x (kNT x 16) columns
-        f32x4 s[2][kNT];
+      for (int kt = 0; kt < kKT / 16; ++kt) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int j = 0; j < kNT; ++j) s[kt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const char* arow = ks_lds + (kt * 16 + col) * GG::KROW + grp * 16;
 #pragma unroll
-          for (int j = 0; j < kNT; ++j) s[kt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const char* arow = ks_lds + (sub * 32 + kt * 16 + col) * GG::KROW + grp * 16;
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const bf16x8 av =
+              __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + ks * 64));
 #pragma unroll
-          for (int ks = 0; ks < KSTEPS; ++ks) {
-            const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + ks * 64));
+          for (int j = 0; j < kNT; ++j)
+            s[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[j][ks], s[kt][j], 0, 0, 0);
+        }
+      }
+      // ---- online softmax per column over the 64 keys; P^T operands for the
+      // two 32-key products (lane order of key_slot within each half)
+      bf16x8 pf[kNT][kKT / 32];
 #pragma unroll
-            for (int j = 0; j < kNT; ++j)
-              s[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[j][ks], s[kt][j], 0, 0, 0);
+      for (int j = 0; j < kNT; ++j) {
+        const int qpos = off + pbase[j] + col;  // absolute position of this column's query
+        float sv[kKT / 4];
+#pragma unroll
+        for (int kt = 0; kt < kKT / 16; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[kt * 4 + i] = s[kt][j][i];
+        if (key0 + kKT - 1 > off + pbase[j]) {  // the stage crosses some column's diagonal
+#pragma unroll
+          for (int i = 0; i < kKT / 4; ++i) {
+            const int kpos = key0 + (i >> 2) * 16 + grp * 4 + (i & 3);
+            if (kpos > qpos) sv[i] = -INFINITY;
           }
         }
-        // ---- online softmax per column; build P^T operands
-        bf16x8 pf[kNT];
+        float mx = sv[0];
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-          const int qpos = off + pbase[j] + col;  // absolute position of this column's query
-          float sv[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sv[i] = s[0][j][i];
-            sv[4 + i] = s[1][j][i];
-          }
-          if (key0 + 31 > off + pbase[j]) {  // the step crosses some column's diagonal
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int kpos = key0 + (i >> 2) * 16 + grp * 4 + (i & 3);
-              if (kpos > qpos) sv[i] = -INFINITY;
-            }
-          }
-          float mx = sv[0];
-#pragma unroll
-          for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-          mx = fmaxf(mx, xor_lane(mx, 16));
-          mx = fmaxf(mx, xor_lane(mx, 32));
-          mx *= a.scale_log2;
+        for (int i = 1; i < kKT / 4; ++i) mx = fmaxf(mx, sv[i]);
+        mx = fmaxf(mx, xor_lane(mx, 16));
+        mx = fmaxf(mx, xor_lane(mx, 32));
+        mx *= a.scale_log2;
 #if PA_PREFILL_LAZY
-          // all lanes of a column see the same mx and m, so they agree on it
-          if (mx > m[j] + kLazyLog2) {
+        // all lanes of a column see the same mx and m, so they agree on it
+        if (mx > m[j] + kLazyLog2) {
 #else
-          {
+        {
 #endif
-            const float mnew = fmaxf(m[j], mx);
-            const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);  // 0 on the first step
-            m[j] = mnew;
-            l[j] *= alpha;
+          const float mnew = fmaxf(m[j], mx);
+          const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);  // 0 on the first step
+          m[j] = mnew;
+          l[j] *= alpha;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) o[j][mt] *= alpha;
-          }
-          const float msafe = (m[j] == -INFINITY) ? 0.f : m[j];
+          for (int mt = 0; mt < MT; ++mt) o[j][mt] *= alpha;
+        }
+        const float negm = (m[j] == -INFINITY) ? 0.f : -m[j];
+#pragma unroll
+        for (int h = 0; h < kKT / 32; ++h) {
           float p[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sv[i], a.scale_log2, -msafe));
+          for (int i = 0; i < 8; ++i)
+            p[i] = __builtin_amdgcn_exp2f(fmaf(sv[h * 8 + i], a.scale_log2, negm));
           uint4 pk;
           pk.x = pack2_bf16(p[0], p[1]);
           pk.y = pack2_bf16(p[2], p[3]);
           pk.z = pack2_bf16(p[4], p[5]);
           pk.w = pack2_bf16(p[6], p[7]);
-          // the sum adds the rounded weights the MFMA sees: an exact weighted mean
-          l[j] += (bf16_lo(pk.x) + bf16_hi(pk.x)) + (bf16_lo(pk.y) + bf16_hi(pk.y)) +
-                  (bf16_lo(pk.z) + bf16_hi(pk.z)) + (bf16_lo(pk.w) + bf16_hi(pk.w));
-          pf[j] = __builtin_bit_cast(bf16x8, pk);
+          // the sum adds the rounded weights the MFMA sees (an exact weighted
+          // mean): a dot product of each packed pair with (1, 1)
+          l[j] = sum_pair_bf16(pk.x, l[j]);
+          l[j] = sum_pair_bf16(pk.y, l[j]);
+          l[j] = sum_pair_bf16(pk.z, l[j]);
+          l[j] = sum_pair_bf16(pk.w, l[j]);
+          pf[j][h] = __builtin_bit_cast(bf16x8, pk);
         }
-        // ---- O^T += V^T P^T
+      }
+      // ---- O^T += V^T P^T, two 32-key products
+#pragma unroll
+      for (int h = 0; h < kKT / 32; ++h) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const char* vrow = vt_lds + (mt * 16 + col) * GG::VROW + (sub * 32 + grp * 8) * 2;
+          const char* vrow = vt_lds + (mt * 16 + col) * GG::VROW + (h * 32 + grp * 8) * 2;
           const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vrow));
 #pragma unroll
           for (int j = 0; j < kNT; ++j)
-            o[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf[j], o[j][mt], 0, 0, 0);
+            o[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf[j][h], o[j][mt], 0, 0, 0);
         }
       }
+    }
 
     if (st + 1 < n_stages) store_stage<D>(lds + ((st + 1) & 1) * GG::STAGE, kready, vready);
     __syncthreads();
