@@ -162,6 +162,63 @@ def run_prefill(args, torch, B, W, dev):
     }
 
 
+def run_mixed(args, torch, B, W, dev):
+    """A mixed step (decode rows + chunked-prefill rows) in one varlen launch."""
+    import numpy as np
+    case = W.make_case("mixed")
+    slots, cu_q, cu_k = B.pa_build_metadata(case.block_tables, case.starts, case.ends,
+                                            case.block_size)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bf(a):
+        return t(a.view(np.int16)).view(torch.bfloat16)
+
+    kc, vc = bf(case.k_cache), bf(case.v_cache)
+    k_new, v_new, q = bf(case.k_new), bf(case.v_new), bf(case.q)
+    out = torch.empty_like(q)
+    slots_d, cuq_d, cuk_d, bt_d = t(slots), t(cu_q), t(cu_k), t(case.block_tables)
+    qlens = case.ends - case.starts
+    mq, mk = int(qlens.max()), int(case.ends.max())
+
+    n_dec = case.meta["decode_rows"]
+    ws = torch.empty(max(16, B.load().pa_mixed_workspace_size(
+        B.ctypes.byref(B._desc_from_cache(kc, case.num_q_heads)), n_dec, mk)),
+        dtype=torch.uint8, device=dev)
+
+    def step_mixed():
+        B.pa_store_kv(k_new, v_new, kc, vc, slots_d)
+        B.pa_mixed_varlen(q, kc, vc, cuq_d, cuk_d, n_dec, mq, mk, bt_d, case.scale, out,
+                          workspace=ws)
+
+    def step_prefill_only():
+        B.pa_store_kv(k_new, v_new, kc, vc, slots_d)
+        B.pa_prefill_varlen(q, kc, vc, cuq_d, cuk_d, mq, mk, bt_d, case.scale, out)
+
+    def timed(step):
+        for _ in range(max(1, args.warmup)):
+            step()
+        torch.cuda.synchronize(dev)
+        n = max(3, args.steps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            step()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(step_mixed)
+    ms_single = timed(step_prefill_only)
+    kv = int(case.ends.astype(np.int64).sum()) * case.num_kv_heads * case.head_dim * 4
+    return {"workload": W.DESCRIPTIONS["mixed"], "q_tokens": int(qlens.sum()),
+            "entry": "pa_store_kv + pa_mixed_varlen",
+            "ms_per_step": round(ms, 4), "kv_GBps": round(kv / (ms * 1e-3) / 1e9, 1),
+            "q_tokens_per_s": round(int(qlens.sum()) / (ms * 1e-3), 1),
+            "ms_per_step_single_prefill_launch": round(ms_single, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +228,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--prefill", action="store_true", help="also time the prefill workload")
+    ap.add_argument("--mixed", action="store_true",
+                    help="also time a mixed decode + chunked-prefill varlen step")
     ap.add_argument("--mode", default="separate", choices=["fused", "separate"],
                     help="fused: pa_decode_step (store + decode in one pass); separate: "
                          "pa_store_kv then pa_decode")
@@ -329,6 +388,8 @@ def main() -> int:
     }
     if args.prefill:
         rec["prefill"] = run_prefill(args, torch, B, W, dev)
+    if args.mixed:
+        rec["mixed"] = run_mixed(args, torch, B, W, dev)
     if args.cpu_budget > 0:
         rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
     else:

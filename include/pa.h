@@ -196,6 +196,31 @@ int pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
                       void* out, const pa_desc* desc, void* stream);
 
 /*
+ * pa_mixed_varlen -- one varlen step that mixes decode rows and prefill rows
+ * (decode sequences first, then new or chunked prompts: the mixed batch of a
+ * token-budget scheduler; "对照 Nano-vLLM 实现：读懂 vLLM 调度" §2, and the
+ * chunk that starts mid-block of "Nano-vLLM 源码解读 - 3. PagedAttention" §4).
+ *
+ * Same inputs and result as pa_prefill_varlen over all num_seqs sequences,
+ * with one extra precondition: the first num_decode_rows sequences have
+ * q_len = 1 (cu_seqlens_q[b] = b for b <= num_decode_rows). Those rows run
+ * through the split-K decode kernels (k_len from cu_seqlens_k), the rest
+ * through the prefill kernel, one launch each on `stream`.
+ *
+ *   num_decode_rows  0 <= num_decode_rows <= num_seqs.
+ *   workspace     device, >= pa_mixed_workspace_size(desc, num_decode_rows,
+ *                 max_seqlen_k) bytes (may be NULL when that is 0).
+ */
+size_t pa_mixed_workspace_size(const pa_desc* desc, int32_t num_decode_rows,
+                               int32_t max_seqlen_k);
+int pa_mixed_varlen(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                    int32_t num_decode_rows, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq, float scale,
+                    void* out, void* workspace, size_t workspace_bytes, const pa_desc* desc,
+                    void* stream);
+
+/*
  * pa_build_metadata -- host-side step metadata ([P5 §4]; [P2]
  * prepare_prefill / prepare_decode). Runs on the CPU, reads host memory only.
  *

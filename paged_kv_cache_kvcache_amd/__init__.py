@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     pa_decode,
     pa_decode_step,
     pa_decode_workspace_size,
+    pa_mixed_varlen,
     pa_prefill_varlen,
     pa_store_kv,
 )

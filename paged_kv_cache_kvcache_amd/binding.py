@@ -25,7 +25,7 @@ PA_ERR_HIP = -4
 # Every symbol include/pa.h declares (checked by the CPU test suite).
 EXPORTS = (
     "pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_partitioned",
-    "pa_decode_step",
+    "pa_decode_step", "pa_mixed_varlen", "pa_mixed_workspace_size",
     "pa_decode_workspace_size_ex", "pa_prefill_varlen", "pa_build_metadata",
     "pa_last_error", "pa_version",
 )
@@ -84,6 +84,11 @@ def load():
     lib.pa_prefill_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, f32, vp, pdesc,
                                       vp]
     lib.pa_prefill_varlen.restype = ctypes.c_int
+    lib.pa_mixed_workspace_size.argtypes = [pdesc, i32, i32]
+    lib.pa_mixed_workspace_size.restype = sz
+    lib.pa_mixed_varlen.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, i32, f32, vp, vp,
+                                    sz, pdesc, vp]
+    lib.pa_mixed_varlen.restype = ctypes.c_int
     lib.pa_build_metadata.argtypes = [vp, i32, vp, vp, i32, i32, vp, i64, vp, vp]
     lib.pa_build_metadata.restype = ctypes.c_int64
     lib.pa_last_error.argtypes = []
@@ -268,6 +273,43 @@ def pa_prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, max_seqle
                                     int(max_seqlen_q), int(max_seqlen_k), block_tables.data_ptr(),
                                     int(block_tables.shape[1]), float(scale), out.data_ptr(),
                                     ctypes.byref(desc), _stream(q)))
+
+
+def pa_mixed_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, num_decode_rows: int,
+                    max_seqlen_q: int, max_seqlen_k: int, block_tables, scale: float, out,
+                    workspace=None) -> None:
+    """Varlen step whose first ``num_decode_rows`` sequences have one query
+    each (decode rows, run by the split-K decode kernels) followed by prefill
+    rows (run by the MFMA prefill kernel)."""
+    import torch
+    _need_cuda(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_tables, out)
+    _check_cache_pair(k_cache, v_cache)
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bf16")
+    for t in (cu_seqlens_q, cu_seqlens_k, block_tables):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("metadata must be contiguous int32")
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous")
+    total_q, h_q, d = q.shape
+    if tuple(out.shape) != (total_q, h_q, d) or d != k_cache.shape[3]:
+        raise ValueError("shape mismatch between q, out and the cache")
+    num_seqs = int(cu_seqlens_q.numel()) - 1
+    if num_seqs < 0 or cu_seqlens_k.numel() != num_seqs + 1 or block_tables.shape[0] != num_seqs:
+        raise ValueError("cu_seqlens must be [batch+1] and block_tables [batch, max_blocks]")
+    desc = _desc_from_cache(k_cache, h_q)
+    lib = load()
+    need = int(lib.pa_mixed_workspace_size(ctypes.byref(desc), int(num_decode_rows),
+                                           int(max_seqlen_k)))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_mixed_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                               cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), num_seqs,
+                               int(num_decode_rows), int(max_seqlen_q), int(max_seqlen_k),
+                               block_tables.data_ptr(), int(block_tables.shape[1]), float(scale),
+                               out.data_ptr(), ws_ptr, ws_bytes, ctypes.byref(desc), _stream(q)))
 
 
 def pa_build_metadata(block_tables: np.ndarray, starts, ends, block_size: int):

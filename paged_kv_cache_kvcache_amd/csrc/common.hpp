@@ -30,6 +30,26 @@ inline int launch_status(const char* what) {
   return PA_OK;
 }
 
+// ------------------------------------------------- decode launch (decode.hip)
+
+struct NewTokens {  // the fused store's inputs (null for plain decode)
+  const void* k;
+  int64_t k_stride;
+  const void* v;
+  int64_t v_stride;
+  const int32_t* slot_mapping;
+};
+
+// Split-K decode of num_seqs rows; lengths from context_lens, or (when it is
+// null) from cu_k[b+1] - cu_k[b]. Validates its arguments; returns a status.
+int launch_decode(const char* who, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, const int32_t* cu_k, int32_t num_seqs,
+                  int32_t max_context_len, float scale, void* out, void* workspace,
+                  size_t workspace_bytes, int32_t partition_blocks, const pa_desc* desc,
+                  void* stream, const NewTokens* nt);
+size_t decode_workspace_bytes(const pa_desc* desc, int32_t num_seqs, int32_t max_context_len);
+
 // ------------------------------------------------------------- bf16 bits
 
 // bf16 -> fp32 is exact: the bf16 pattern is the top half of the fp32 one.

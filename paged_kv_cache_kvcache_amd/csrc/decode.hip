@@ -41,7 +41,8 @@ struct DecodeArgs {
   const uint16_t* k_cache;
   const uint16_t* v_cache;
   const int32_t* block_tables;
-  const int32_t* context_lens;
+  const int32_t* context_lens;  // null: lengths are cu_k[b+1] - cu_k[b]
+  const int32_t* cu_k;
   float* ws_o;   // [num_seqs, H_q, max_parts, d] fp32 unnormalised partial outputs
   float* ws_ml;  // [num_seqs, H_q, max_parts, 2]  (running max in log2 units, sum)
   uint16_t* out;
@@ -74,6 +75,10 @@ __device__ __forceinline__ float dot8_bf16(const uint4& k, const uint32_t (&q)[4
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, k.w),
                                         __builtin_bit_cast(bf16x2, q[3]), acc, false);
   return acc;
+}
+
+__device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
+  return a.context_lens ? a.context_lens[b] : a.cu_k[b + 1] - a.cu_k[b];
 }
 
 __device__ __forceinline__ int clamp_len(int n, int max_blocks) {
@@ -272,7 +277,7 @@ void decode_split_kernel(DecodeArgs a) {
   const int sub = lane % LPT;  // which 8 elements of the head vector
   const int row = lane / LPT;  // which token of a load instruction
 
-  const int n = clamp_len(a.context_lens[b], a.max_blocks);
+  const int n = clamp_len(seq_len(a, b), a.max_blocks);
   const int nparts = min((n + a.part_tokens - 1) / a.part_tokens, a.max_parts);
   const int64_t head0 = (int64_t)b * H_q + (int64_t)g * G;  // first q-head of the group
 
@@ -430,7 +435,7 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a, int 
   constexpr int EPL = D / kWave;  // output elements per lane
   const int h = blockIdx.x % H_q;
   const int b = blockIdx.x / H_q;
-  const int n = clamp_len(a.context_lens[b], a.max_blocks);
+  const int n = clamp_len(seq_len(a, b), a.max_blocks);
   const int nparts = min((n + a.part_tokens - 1) / a.part_tokens, a.max_parts);
   if (nparts <= 1) return;
   const int64_t w0 = ((int64_t)b * H_q + h) * a.max_parts;
@@ -506,17 +511,12 @@ Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part
   return p;
 }
 
-struct NewTokens {  // the fused store's inputs (all null for plain decode)
-  const void* k;
-  int64_t k_stride;
-  const void* v;
-  int64_t v_stride;
-  const int32_t* slot_mapping;
-};
+}  // namespace
 
 int launch_decode(const char* who, const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_tables, int32_t max_blocks_per_seq,
-                  const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                  const int32_t* context_lens, const int32_t* cu_k, int32_t num_seqs,
+                  int32_t max_context_len,
                   float scale, void* out, void* workspace, size_t workspace_bytes,
                   int32_t partition_blocks, const pa_desc* desc, void* stream,
                   const NewTokens* nt) {
@@ -525,7 +525,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || partition_blocks < 0)
     return fail(PA_ERR_INVALID_ARG, "%s: negative size", who);
   if (num_seqs == 0) return PA_OK;
-  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+  if (!q || !k_cache || !v_cache || !block_tables || !(context_lens || cu_k) || !out)
     return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if ((int64_t)max_blocks_per_seq * kBlockSize < max_context_len)
     return fail(PA_ERR_INVALID_ARG, "%s: max_context_len %d exceeds %d table entries", who,
@@ -560,6 +560,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.v_cache = (const uint16_t*)v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.cu_k = cu_k;
   const size_t o_floats = (size_t)num_seqs * desc->num_q_heads * plan.max_parts * D;
   a.ws_o = plan.ws_bytes ? (float*)workspace : nullptr;
   a.ws_ml = plan.ws_bytes ? (float*)workspace + o_floats : nullptr;
@@ -599,7 +600,11 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   return PA_OK;
 }
 
-}  // namespace
+size_t decode_workspace_bytes(const pa_desc* desc, int32_t num_seqs, int32_t max_context_len) {
+  if (check_desc(desc) != PA_OK || num_seqs < 0 || max_context_len < 0) return 0;
+  return make_plan(desc, num_seqs, max_context_len, 0).ws_bytes;
+}
+
 }  // namespace pa
 
 extern "C" size_t pa_decode_workspace_size_ex(const pa_desc* desc, int32_t num_seqs,
@@ -623,7 +628,7 @@ extern "C" int pa_decode_partitioned(const void* q, const void* k_cache, const v
                                      int32_t partition_blocks, const pa_desc* desc,
                                      void* stream) {
   return pa::launch_decode("pa_decode", q, k_cache, v_cache, block_tables, max_blocks_per_seq,
-                           context_lens, num_seqs, max_context_len, scale, out, workspace,
+                           context_lens, nullptr, num_seqs, max_context_len, scale, out, workspace,
                            workspace_bytes, partition_blocks, desc, stream, nullptr);
 }
 
@@ -646,6 +651,7 @@ extern "C" int pa_decode_step(const void* q, const void* k_new, int64_t k_row_st
                               size_t workspace_bytes, const pa_desc* desc, void* stream) {
   const pa::NewTokens nt{k_new, k_row_stride, v_new, v_row_stride, slot_mapping};
   return pa::launch_decode("pa_decode_step", q, k_cache, v_cache, block_tables,
-                           max_blocks_per_seq, context_lens, num_seqs, max_context_len, scale,
+                           max_blocks_per_seq, context_lens, nullptr, num_seqs, max_context_len,
+                           scale,
                            out, workspace, workspace_bytes, 0, desc, stream, &nt);
 }

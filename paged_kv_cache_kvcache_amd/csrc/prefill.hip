@@ -409,32 +409,35 @@ PrefillFn pick(int G) {
 }  // namespace
 }  // namespace pa
 
-extern "C" int pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                 float scale, void* out, const pa_desc* desc, void* stream) {
-  using namespace pa;
+namespace pa {
+namespace {
+
+int launch_prefill(const char* who, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                   int32_t max_seqlen_q, int32_t max_seqlen_k, const int32_t* block_tables,
+                   int32_t max_blocks_per_seq, float scale, void* out, const pa_desc* desc,
+                   void* stream) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_blocks_per_seq < 0)
-    return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: negative size");
+    return fail(PA_ERR_INVALID_ARG, "%s: negative size", who);
   if (num_seqs == 0 || max_seqlen_q == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_tables || !out)
-    return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: NULL pointer");
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if (max_seqlen_q > max_seqlen_k)
-    return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: max_seqlen_q %d > max_seqlen_k %d",
-                max_seqlen_q, max_seqlen_k);
+    return fail(PA_ERR_INVALID_ARG, "%s: max_seqlen_q %d > max_seqlen_k %d", who, max_seqlen_q,
+                max_seqlen_k);
   if ((int64_t)max_blocks_per_seq * kBlockSize < max_seqlen_k)
-    return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: max_seqlen_k %d exceeds %d table entries",
+    return fail(PA_ERR_INVALID_ARG, "%s: max_seqlen_k %d exceeds %d table entries", who,
                 max_seqlen_k, max_blocks_per_seq);
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15u)
-    return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: q, caches and out must be 16-byte aligned");
+    return fail(PA_ERR_INVALID_ARG, "%s: q, caches and out must be 16-byte aligned", who);
   const int G = desc->num_q_heads / desc->num_kv_heads;
   const int D = desc->head_dim;
-  const int QB = 16 * kNT * kWaves / G;
-  const int64_t blocks = (int64_t)num_seqs * desc->num_kv_heads * ((max_seqlen_q + QB - 1) / QB);
-  if (blocks > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "pa_prefill_varlen: grid too large");
+  const int QB = kCols / G;
+  const int64_t rblocks = (max_seqlen_q + QB - 1) / QB;
+  const int64_t blocks = (int64_t)num_seqs * desc->num_kv_heads * rblocks;
+  if (blocks > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "%s: grid too large", who);
 
   PrefillArgs a;
   a.q = (const uint16_t*)q;
@@ -448,9 +451,61 @@ extern "C" int pa_prefill_varlen(const void* q, const void* k_cache, const void*
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_kv_heads = desc->num_kv_heads;
-  a.max_rblocks = (max_seqlen_q + QB - 1) / QB;
+  a.max_rblocks = (int32_t)rblocks;
   a.scale_log2 = scale * kLog2e;
   PrefillFn fn = D == 128 ? pick<128>(G) : pick<64>(G);
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a);
-  return launch_status("pa_prefill_varlen");
+  return launch_status(who);
+}
+
+}  // namespace
+}  // namespace pa
+
+extern "C" int pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 float scale, void* out, const pa_desc* desc, void* stream) {
+  return pa::launch_prefill("pa_prefill_varlen", q, k_cache, v_cache, cu_seqlens_q,
+                            cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, block_tables,
+                            max_blocks_per_seq, scale, out, desc, stream);
+}
+
+extern "C" size_t pa_mixed_workspace_size(const pa_desc* desc, int32_t num_decode_rows,
+                                          int32_t max_seqlen_k) {
+  return pa::decode_workspace_bytes(desc, num_decode_rows, max_seqlen_k);
+}
+
+// The first num_decode_rows sequences of the varlen batch have one query
+// each: they go through the split-K decode kernels (lengths from
+// cu_seqlens_k); the remaining rows go through the MFMA prefill kernel.
+extern "C" int pa_mixed_varlen(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               int32_t num_seqs, int32_t num_decode_rows, int32_t max_seqlen_q,
+                               int32_t max_seqlen_k, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, float scale, void* out,
+                               void* workspace, size_t workspace_bytes, const pa_desc* desc,
+                               void* stream) {
+  using namespace pa;
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (num_decode_rows < 0 || num_decode_rows > num_seqs)
+    return fail(PA_ERR_INVALID_ARG, "pa_mixed_varlen: num_decode_rows %d outside [0, %d]",
+                num_decode_rows, num_seqs);
+  if (num_decode_rows > 0) {
+    rc = launch_decode("pa_mixed_varlen", q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       nullptr, cu_seqlens_k, num_decode_rows, max_seqlen_k, scale, out,
+                       workspace, workspace_bytes, 0, desc, stream, nullptr);
+    if (rc) return rc;
+  }
+  const int32_t rest = num_seqs - num_decode_rows;
+  if (rest > 0) {
+    if (!cu_seqlens_q || !cu_seqlens_k || !block_tables)
+      return fail(PA_ERR_INVALID_ARG, "pa_mixed_varlen: NULL pointer");
+    rc = launch_prefill("pa_mixed_varlen", q, k_cache, v_cache, cu_seqlens_q + num_decode_rows,
+                        cu_seqlens_k + num_decode_rows, rest, max_seqlen_q, max_seqlen_k,
+                        block_tables + (int64_t)num_decode_rows * max_blocks_per_seq,
+                        max_blocks_per_seq, scale, out, desc, stream);
+  }
+  return rc;
 }

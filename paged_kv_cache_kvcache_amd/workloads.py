@@ -219,9 +219,47 @@ def prefill_case(num_q_heads: int, num_kv_heads: int, head_dim: int, prefix_len:
                        {"prefix_len": prefix_len, "shared_prefix_blocks": shared})
 
 
+def mixed_case(num_q_heads: int, num_kv_heads: int, head_dim: int, decode_lens, chunks,
+               seed: int, block_size: int = BLOCK_SIZE, name: str = "mixed",
+               threads: int | None = None) -> PrefillCase:
+    """One mixed step: decode rows (one new token at position len-1 of a
+    sequence of ``len`` tokens) followed by chunked-prefill rows, each given
+    as ``(cached, chunk)``: positions ``cached .. cached+chunk-1`` are new
+    (``cached`` need not be block-aligned). Every sequence owns its blocks,
+    which cover all ``end`` positions."""
+    rng = np.random.default_rng(seed)
+    starts, ends = [], []
+    for n in decode_lens:
+        starts.append(int(n) - 1)
+        ends.append(int(n))
+    for cached, chunk in chunks:
+        starts.append(int(cached))
+        ends.append(int(cached) + int(chunk))
+    starts = np.asarray(starts, dtype=np.int32)
+    ends = np.asarray(ends, dtype=np.int32)
+    need = [blocks_needed(e, block_size) for e in ends.tolist()]
+    num_blocks = max(1, math.ceil(1.1 * sum(need)))
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    tables, pos = [], 0
+    for n in need:
+        tables.append(perm[pos:pos + n].tolist())
+        pos += n
+    total_q = int((ends - starts).sum())
+    q = normal_bf16(rng, (total_q, num_q_heads, head_dim))
+    k_new = normal_bf16(rng, (total_q, num_kv_heads, head_dim))
+    v_new = normal_bf16(rng, (total_q, num_kv_heads, head_dim))
+    k_cache = pool_bf16(num_blocks, block_size, num_kv_heads, head_dim, seed, 0, threads)
+    v_cache = pool_bf16(num_blocks, block_size, num_kv_heads, head_dim, seed, 1, threads)
+    return PrefillCase(name, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       q, k_new, v_new, k_cache, v_cache, pad_tables(tables), starts, ends,
+                       1.0 / math.sqrt(head_dim), seed,
+                       {"decode_rows": len(decode_lens), "prefill_rows": len(chunks)})
+
+
 # ------------------------------------------------------------ named workloads
 
-SEEDS = {"tiny": 1001, "qwen3-0.6b": 1002, "qwen3-8b": 1003, "long": 1004, "prefill": 1005}
+SEEDS = {"tiny": 1001, "qwen3-0.6b": 1002, "qwen3-8b": 1003, "long": 1004, "prefill": 1005,
+         "mixed": 1006}
 
 DESCRIPTIONS = {
     "tiny": "decode, 4 q / 2 kv heads, d 64, B 256, pool 16, ctx {1,17,256,300}",
@@ -230,6 +268,9 @@ DESCRIPTIONS = {
     "long": "decode, 32 q / 8 kv heads, d 128, B 256, 32 seqs at ctx 16384",
     "prefill": "varlen causal prefill, 32 q / 8 kv heads, d 128, B 256, 16 prompts: "
                "shared 1024-token prefix + suffix U[100,2000]",
+    "mixed": "mixed varlen step, 32 q / 8 kv heads, d 128, B 256: 224 decode rows "
+             "(ctx U[512,8192]) + 4 chunked-prefill rows of 512 tokens starting mid-block "
+             "(cached U[100,4000])",
 }
 
 
@@ -250,4 +291,10 @@ def make_case(name: str, seed: int | None = None, threads: int | None = None):
     if name == "prefill":
         suffix = np.random.default_rng(seed).integers(100, 2000 + 1, size=16)
         return prefill_case(32, 8, 128, 1024, suffix, seed + 1, name=name, threads=threads)
+    if name == "mixed":
+        rng = np.random.default_rng(seed)
+        dec = rng.integers(512, 8192 + 1, size=224)
+        cached = rng.integers(100, 4000 + 1, size=4)
+        return mixed_case(32, 8, 128, dec, [(int(c), 512) for c in cached], seed + 1,
+                          name=name, threads=threads)
     raise KeyError(name)

@@ -146,3 +146,40 @@ def test_full_prompt_without_cache_shares_prefix_rows():
     ref = oracle.prefill_varlen(case.q, kref, vref, cu_q, cu_k, case.block_tables, case.scale,
                                 seqs=[0])
     assert_close(out[cu_q[0]:cu_q[1]], ref[cu_q[0]:cu_q[1]], "full prompt")
+
+
+@pytest.mark.parametrize("entry", ["pa_prefill_varlen", "pa_mixed_varlen"])
+def test_mixed_decode_and_chunked_prefill_batch(entry):
+    """A varlen step holding decode rows (q_len 1, first) and chunked-prefill
+    rows whose cached prefix ends mid-block (the mixed step of a token-budget
+    scheduler), through the plain prefill entry and through pa_mixed_varlen
+    (decode rows on the split-K decode kernels); sampled rows vs the oracle."""
+    case = W.make_case("mixed")
+    if entry == "pa_prefill_varlen":
+        out, kref, vref, cu_q, cu_k = run_prefill_step(case)
+    else:
+        slots, cu_q, cu_k = B.pa_build_metadata(case.block_tables, case.starts, case.ends, 256)
+        kc, vc = dev_bf16(case.k_cache), dev_bf16(case.v_cache)
+        B.pa_store_kv(dev_bf16(case.k_new), dev_bf16(case.v_new), kc, vc, dev_i32(slots))
+        q = dev_bf16(case.q)
+        o = torch.empty_like(q)
+        qlens = case.ends - case.starts
+        B.pa_mixed_varlen(q, kc, vc, dev_i32(cu_q), dev_i32(cu_k), case.meta["decode_rows"],
+                          int(qlens.max()), int(case.ends.max()), dev_i32(case.block_tables),
+                          case.scale, o)
+        torch.cuda.synchronize()
+        out = host_f64(o)
+        kref, vref = oracle.store_kv(case.k_cache, case.v_cache, case.k_new, case.v_new, slots)
+    rng = np.random.default_rng(4)
+    got, ref = [], []
+    n_dec = case.meta["decode_rows"]
+    for b in list(rng.choice(n_dec, 12, replace=False)) + list(range(n_dec, case.batch)):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        n = q1 - q0
+        rows = sorted(set([0, n - 1]) | set(rng.integers(0, n, 6).tolist()))
+        r = oracle.prefill_one(case.q[q0:q1], kref, vref, case.block_tables[b],
+                               int(case.ends[b]), case.scale, query_rows=rows)
+        got.append(out[q0:q1][rows])
+        ref.append(r[rows])
+    mx, mean = assert_close(np.concatenate(got), np.concatenate(ref), "mixed batch")
+    print("  parity mixed batch (%s): max abs %.3g mean abs %.3g" % (entry, mx, mean))
