@@ -243,6 +243,75 @@ int64_t pa_build_metadata(const int32_t* block_tables, int32_t max_blocks_per_se
                           int32_t block_size, int32_t* slot_mapping, int64_t slot_capacity,
                           int32_t* cu_seqlens_q, int32_t* cu_seqlens_k);
 
+/*
+ * Block manager -- host-side allocator of the physical blocks, with a
+ * chained-hash prefix cache ([P1 §12.8] BlockManager; the worked trace of
+ * "对照 Nano-vLLM 实现：读懂 vLLM 调度" §1.2). It produces the block tables
+ * (and, through pa_build_metadata, the slots) that the kernels consume.
+ * Host memory only; not thread-safe (one caller at a time per manager).
+ *
+ * State: per block a reference count, the prefix hash of its contents and
+ * those token ids; a FIFO of free blocks (taken from the front, returned to
+ * the back); an index from prefix hash to block. A full block's hash is
+ * xxh64 (seed 0) of the previous block's hash as 8 little-endian bytes (none
+ * for block 0) followed by its token ids as int64 little endian. Freeing keeps
+ * a block's hash and index entry; handing the block out again drops them.
+ * A sequence is held by the caller: its token ids (int64), its block table
+ * and how many of its tokens are cached.
+ *
+ * Return values: >= 0 as documented, or a negative PA_ERR_* code.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* num_blocks >= 1, block_size >= 1; NULL on bad arguments. */
+pa_block_manager* pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* xxh64 of (prefix as 8 LE bytes if has_prefix) + token_ids[0..n) as int64 LE. */
+uint64_t pa_bm_chained_hash(const int64_t* token_ids, int32_t n, uint64_t prefix,
+                            int32_t has_prefix);
+
+/* Writes to *num_cached_blocks the leading blocks of the prompt (all but its
+ * last block) found in the index with identical tokens; returns 1 if the free
+ * FIFO can hold the blocks that are not cached-and-in-use, else 0. */
+int32_t pa_bm_can_allocate(pa_block_manager* bm, const int64_t* token_ids, int32_t num_tokens,
+                           int32_t* num_cached_blocks);
+
+/* Fill block_table (capacity >= ceil(num_tokens / block_size)): the first
+ * num_cached_blocks from the index (shared: count + 1; freed: revived), the
+ * rest from the free FIFO. Returns the number of blocks; the caller's cached
+ * token count becomes num_cached_blocks * block_size. */
+int32_t pa_bm_allocate(pa_block_manager* bm, const int64_t* token_ids, int32_t num_tokens,
+                       int32_t num_cached_blocks, int32_t* block_table, int32_t capacity);
+
+/* Drop one reference to each block, last to first; blocks reaching zero go
+ * to the back of the free FIFO. */
+int32_t pa_bm_deallocate(pa_block_manager* bm, const int32_t* block_table, int32_t n_blocks);
+
+/* 1 if a sequence of seq_len tokens (its newest included) can grow: it needs
+ * a free block exactly when seq_len % block_size == 1. */
+int32_t pa_bm_can_append(const pa_block_manager* bm, int32_t seq_len);
+
+/* Append a block from the free FIFO when seq_len % block_size == 1; returns
+ * the new number of blocks. */
+int32_t pa_bm_may_append(pa_block_manager* bm, int32_t seq_len, int32_t* block_table,
+                         int32_t n_blocks, int32_t capacity);
+
+/* After a step computed num_scheduled_tokens tokens past num_cached_tokens:
+ * hash and index the blocks that became full. Returns how many. */
+int32_t pa_bm_hash_blocks(pa_block_manager* bm, const int64_t* token_ids, int32_t num_tokens,
+                          const int32_t* block_table, int32_t n_blocks,
+                          int32_t num_cached_tokens, int32_t num_scheduled_tokens);
+
+/* Inspection. */
+int32_t pa_bm_num_free(const pa_block_manager* bm);
+int32_t pa_bm_free_list(const pa_block_manager* bm, int32_t* out, int32_t capacity);
+int32_t pa_bm_block_state(const pa_block_manager* bm, int32_t block_id, int32_t* ref_count,
+                          uint64_t* hash, int32_t* hashed);
+int32_t pa_bm_lookup(const pa_block_manager* bm, uint64_t hash);
+int32_t pa_bm_index_entries(const pa_block_manager* bm, uint64_t* hashes, int32_t* block_ids,
+                            int32_t capacity);
+
 /* Message for the last nonzero status returned on this thread ("" if none). */
 const char* pa_last_error(void);
 

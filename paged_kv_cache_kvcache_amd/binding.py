@@ -28,6 +28,10 @@ EXPORTS = (
     "pa_decode_step", "pa_mixed_varlen", "pa_mixed_workspace_size",
     "pa_decode_workspace_size_ex", "pa_prefill_varlen", "pa_build_metadata",
     "pa_last_error", "pa_version",
+    "pa_bm_create", "pa_bm_destroy", "pa_bm_chained_hash", "pa_bm_can_allocate", "pa_bm_allocate",
+    "pa_bm_deallocate", "pa_bm_can_append", "pa_bm_may_append", "pa_bm_hash_blocks",
+    "pa_bm_num_free", "pa_bm_free_list", "pa_bm_block_state", "pa_bm_lookup",
+    "pa_bm_index_entries",
 )
 
 
@@ -91,6 +95,26 @@ def load():
     lib.pa_mixed_varlen.restype = ctypes.c_int
     lib.pa_build_metadata.argtypes = [vp, i32, vp, vp, i32, i32, vp, i64, vp, vp]
     lib.pa_build_metadata.restype = ctypes.c_int64
+    u64 = ctypes.c_uint64
+    lib.pa_bm_create.argtypes = [i32, i32]
+    lib.pa_bm_create.restype = vp
+    lib.pa_bm_destroy.argtypes = [vp]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_chained_hash.argtypes = [vp, i32, u64, i32]
+    lib.pa_bm_chained_hash.restype = u64
+    for name, args in (("pa_bm_can_allocate", [vp, vp, i32, vp]),
+                       ("pa_bm_allocate", [vp, vp, i32, i32, vp, i32]),
+                       ("pa_bm_deallocate", [vp, vp, i32]),
+                       ("pa_bm_can_append", [vp, i32]),
+                       ("pa_bm_may_append", [vp, i32, vp, i32, i32]),
+                       ("pa_bm_hash_blocks", [vp, vp, i32, vp, i32, i32, i32]),
+                       ("pa_bm_num_free", [vp]),
+                       ("pa_bm_free_list", [vp, vp, i32]),
+                       ("pa_bm_block_state", [vp, i32, vp, vp, vp]),
+                       ("pa_bm_lookup", [vp, u64]),
+                       ("pa_bm_index_entries", [vp, vp, vp, i32])):
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = i32
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "store_kv.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "store_kv.hip", "decode.hip", "prefill.hip", "block_manager.cpp"]
 
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
 HIP_FLAGS = [
@@ -57,7 +57,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:

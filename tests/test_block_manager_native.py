@@ -1,0 +1,130 @@
+"""The native block manager (C++ in libpa, CPU only) against the printed
+traces and against the reference allocator on random operation sequences;
+its xxh64 against the xxhash library."""
+
+import time
+
+import numpy as np
+import pytest
+import xxhash
+
+import block_trace as T
+from oracle.block_manager import BlockManager as RefBM, Seq, chained_hash as ref_hash
+from paged_kv_cache_kvcache_amd import binding as B
+from paged_kv_cache_kvcache_amd.block_manager import BlockManager, chained_hash
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    B.load()
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 4, 5, 7, 31, 32, 33, 64, 255, 256, 257, 1000])
+def test_xxh64_matches_library(n):
+    rng = np.random.default_rng(n)
+    t = rng.integers(-2**62, 2**62, size=n)
+    assert chained_hash(t, None) == xxhash.xxh64(t.astype("<i8").tobytes()).intdigest()
+    p = int(rng.integers(0, 2**63))
+    want = xxhash.xxh64(p.to_bytes(8, "little") + t.astype("<i8").tobytes()).intdigest()
+    assert chained_hash(t, p) == want == ref_hash(t, p)
+
+
+def test_trace_of_seven_rounds():
+    T.replay_trace(BlockManager)
+
+
+def test_prefix_hit_and_shared_blocks():
+    T.check_prefix_hit(BlockManager)
+    T.check_shared_blocks(BlockManager)
+
+
+def _same_state(a, b, where):
+    sa, sb = a.state(), b.state()
+    for k in ("free", "used", "ref_count", "hash", "index"):
+        assert sa[k] == sb[k], (where, k)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_operations_match_reference(seed):
+    """Prompts drawn from a few shared prefixes (so the cache hits, misses,
+    revives freed blocks and drops stale entries), chunked prefills, decode
+    steps and frees, applied to both allocators; states compared after every
+    operation."""
+    rng = np.random.default_rng(seed)
+    bs = int(rng.choice([4, 16, 256]))
+    nb = int(rng.integers(6, 40))
+    ref, nat = RefBM(nb, bs), BlockManager(nb, bs)
+    prefixes = [rng.integers(0, 50, size=int(rng.integers(1, 5)) * bs).tolist() for _ in range(3)]
+    live = []  # pairs (ref seq, native seq)
+    for step in range(300):
+        op = rng.integers(0, 4)
+        if op == 0 or not live:  # new prompt
+            p = prefixes[rng.integers(0, 3)] if rng.random() < 0.7 else []
+            cut = int(rng.integers(0, len(p) + 1)) if p else 0
+            toks = p[:cut] + rng.integers(0, 50, size=int(rng.integers(1, 3 * bs))).tolist()
+            a, b = Seq(list(toks), bs), Seq(list(toks), bs)
+            ka, kb = ref.can_allocate(a), nat.can_allocate(b)
+            assert ka == kb, step
+            if ka >= 0:
+                ref.allocate(a, ka)
+                nat.allocate(b, kb)
+                assert a.block_table == b.block_table and a.num_cached_tokens == b.num_cached_tokens
+                live.append((a, b))
+        elif op == 1:  # prefill chunk (or the rest of the prompt)
+            a, b = live[rng.integers(0, len(live))]
+            left = len(a) - a.num_cached_tokens
+            if left > 0:
+                n = int(rng.integers(1, left + 1))
+                ref.hash_blocks(a, n)
+                nat.hash_blocks(b, n)
+                a.num_cached_tokens += n
+                b.num_cached_tokens += n
+        elif op == 2:  # decode step on a fully cached sequence
+            a, b = live[rng.integers(0, len(live))]
+            if a.num_cached_tokens == len(a):
+                t = int(rng.integers(0, 50))
+                a.token_ids.append(t)
+                b.token_ids.append(t)
+                ca, cb = ref.can_append(a), nat.can_append(b)
+                assert ca == cb
+                if ca:
+                    ref.may_append(a)
+                    nat.may_append(b)
+                    assert a.block_table == b.block_table
+                    ref.hash_blocks(a, 1)
+                    nat.hash_blocks(b, 1)
+                    a.num_cached_tokens += 1
+                    b.num_cached_tokens += 1
+                else:
+                    a.token_ids.pop()
+                    b.token_ids.pop()
+        else:  # finish or preempt a sequence
+            i = int(rng.integers(0, len(live)))
+            a, b = live.pop(i)
+            ref.deallocate(a)
+            nat.deallocate(b)
+        _same_state(ref, nat, step)
+
+
+def test_bad_calls_are_rejected():
+    bm = BlockManager(4, 16)
+    s = Seq(list(range(20)), 16)
+    with pytest.raises(B.PAError):
+        bm.deallocate(Seq(list(range(3)), 16, block_table=[2]))
+    with pytest.raises(B.PAError):
+        bm.allocate(s, 1)  # nothing cached yet
+    bm.allocate(s, 0)
+    assert s.block_table == [0, 1]
+
+
+def test_block_hash_cost():
+    """The pages estimate under 1 us of CPU for hashing one 256-token block;
+    report the native figure (and require it to stay well under 50 us)."""
+    t = np.arange(256, dtype=np.int64)
+    n = 2000
+    t0 = time.perf_counter()
+    for i in range(n):
+        chained_hash(t, i)
+    per = (time.perf_counter() - t0) / n
+    print("native chained hash of a 256-token block, incl. the ctypes call: %.2f us" % (per * 1e6))
+    assert per < 50e-6
