@@ -65,16 +65,17 @@ def src_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_src: str, mode: str):
+def traffic_from_profile(kernel_src: str, mode: str, block_size: int = 256):
     """HBM bytes per launch of the dominant call from the committed rocprofv3
     counter summary, or None if it is missing, was taken for another step
-    mode, or on a different kernel source."""
+    mode or block size, or on a different kernel source."""
     try:
         with open(PMC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != src_hash(kernel_src) or rec.get("step_mode") != mode:
+    if (rec.get("source_sha256_16") != src_hash(kernel_src) or rec.get("step_mode") != mode
+            or rec.get("block_size", 256) != block_size):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -235,6 +236,8 @@ def main() -> int:
                          "pa_store_kv then pa_decode")
     ap.add_argument("--graph", action="store_true",
                     help="capture the step in a HIP graph and time its replays")
+    ap.add_argument("--block-size", type=int, default=256,
+                    help="tokens per cache block (power of two, 16..1024); same lengths")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -265,7 +268,7 @@ def main() -> int:
         return 0
 
     B.load()
-    case = W.make_case(args.config)
+    case = W.make_case(args.config, block_size=args.block_size)
 
     def t(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -357,7 +360,7 @@ def main() -> int:
         dom, dom_bytes = "pa_decode", db
         dom_desc = "pa_decode (split-K + merge)"
     dom_gbs = dom_bytes / (ms_call[dom] * 1e-3) / 1e9
-    traffic = traffic_from_profile(DECODE_SRC, args.mode)
+    traffic = traffic_from_profile(DECODE_SRC, args.mode, args.block_size)
 
     rec = {
         "metric": "paged decode: KV GB/s (% HBM peak) + tokens/s at Qwen3-8B shape, batch 256",
@@ -372,9 +375,11 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": W.DESCRIPTIONS[args.config] + "; step = store of the batch's "
+        "config": {"workload": W.DESCRIPTIONS[args.config].replace(
+                       "B 256", "B %d" % case.block_size) + "; step = store of the batch's "
                    "new tokens + decode, one layer", "global_batch": case.batch,
                    "seq_len": max_ctx, "parallelism": "none (1 GPU)",
+                   "block_size": case.block_size,
                    "step_mode": args.mode + (" + hip graph" if args.graph else "")},
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": {"per_layer": round(case.batch / (ms_step * 1e-3), 1),

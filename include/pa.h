@@ -29,7 +29,8 @@
  *     then describes the problem. Host-side checks never read device memory;
  *     device-resident preconditions (slots, table entries, lengths) are the
  *     caller's to keep and are listed per function.
- *   - Supported shapes: head_dim 64 or 128; block_size 256; num_q_heads a
+ *   - Supported shapes: head_dim 64 or 128; block_size a power of two in
+ *     [16, 1024] (256 is the pages' size and the tuned one); num_q_heads a
  *     multiple of num_kv_heads with group size G = num_q_heads / num_kv_heads
  *     in {1, 2, 4, 8}. Others return PA_ERR_UNSUPPORTED.
  */
@@ -54,7 +55,7 @@ typedef struct pa_desc {
   int32_t num_q_heads;  /* H_q                                               */
   int32_t num_kv_heads; /* H_kv; q-head h reads kv-head h / (H_q / H_kv)     */
   int32_t head_dim;     /* d: 64 or 128                                      */
-  int32_t block_size;   /* B: tokens per physical block; 256 ([P5 §5])       */
+  int32_t block_size;   /* B: tokens per physical block; 256 in [P5 §5]      */
   int64_t num_blocks;   /* N: physical blocks in the pool                    */
 } pa_desc;
 
@@ -127,7 +128,8 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
 
 /*
  * pa_decode_partitioned -- pa_decode with an explicit split-K partition of
- * partition_blocks whole blocks per work item (0 = the library's choice,
+ * partition_blocks * 256 tokens per work item, whatever block_size is (whole
+ * blocks at block_size 256; 0 = the library's choice,
  * which is what pa_decode uses). The result is the same attention for any
  * partition size up to rounding. Workspace: pa_decode_workspace_size_ex.
  */

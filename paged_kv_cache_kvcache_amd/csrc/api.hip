@@ -40,8 +40,10 @@ int check_desc(const pa_desc* d) {
                 d->num_q_heads, d->num_kv_heads);
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "head_dim %d not built (64, 128)", d->head_dim);
-  if (d->block_size != kBlockSize)
-    return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (256)", d->block_size);
+  if (d->block_size < kMinBlockSize || d->block_size > kMaxBlockSize ||
+      (d->block_size & (d->block_size - 1)))
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (powers of two, 16..1024)",
+                d->block_size);
   const int g = d->num_q_heads / d->num_kv_heads;
   if (g != 1 && g != 2 && g != 4 && g != 8)
     return fail(PA_ERR_UNSUPPORTED, "GQA group size %d not built (1, 2, 4, 8)", g);

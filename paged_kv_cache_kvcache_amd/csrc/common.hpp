@@ -13,7 +13,9 @@
 namespace pa {
 
 constexpr int kWave = 64;
-constexpr int kBlockSize = 256;  // tokens per physical block the kernels are built for
+constexpr int kMinBlockSize = 16;    // block sizes: powers of two in [16, 1024]
+constexpr int kMaxBlockSize = 1024;
+inline int log2_int(int v) { int s = 0; while ((1 << s) < v) ++s; return s; }
 
 // ------------------------------------------------------------------ errors
 

@@ -8,8 +8,8 @@
 // "Nano-vLLM 源码解读 - 3. PagedAttention", §3).
 //
 // How (MI355X design, not the sketch's):
-//   * split-K: a work item is (sequence, kv-head, partition of whole 256-token
-//     blocks; 4 blocks by default), one wave64 each; a second kernel merges
+//   * split-K: a work item is (sequence, kv-head, partition of 256-token
+//     units; up to 8 units, chosen from the batch), one wave64 each; a second kernel merges
 //     the partitions' (max, sum, unnormalised output) triples exactly.
 //     Sequences that fit one partition are finished by the first kernel.
 //     Items are dispatched highest partition first, so the grid drains on the
@@ -20,7 +20,9 @@
 //     cover one token's 2*d-byte head vector, so a wave instruction reads
 //     64/(d/8) whole token vectors (4 at d = 128). Eight such loads of K and
 //     eight of V are in flight per wave before any arithmetic; full chunks
-//     address them from a wave-uniform base plus one per-lane offset.
+//     address them from a wave-uniform base plus one per-lane offset (one
+//     table lookup per chunk; per group of TPI tokens when blocks are
+//     smaller than a chunk).
 //   * q.k: v_dot2_f32_bf16 on the raw bf16 pairs (exact products, fp32 sum),
 //     then a DPP butterfly over the d/8 lanes of the token (no LDS traffic).
 //   * softmax: base-2 exponent (raw v_exp_f32) with scale*log2(e) folded into
@@ -61,6 +63,8 @@ struct DecodeArgs {
   int32_t num_kv_heads;
   int32_t part_tokens;
   int32_t max_parts;
+  int32_t block_size;   // tokens per physical block (power of two)
+  int32_t block_shift;  // log2(block_size)
   float scale_log2;
 };
 
@@ -81,13 +85,29 @@ __device__ __forceinline__ int seq_len(const DecodeArgs& a, int b) {
   return a.context_lens ? a.context_lens[b] : a.cu_k[b + 1] - a.cu_k[b];
 }
 
-__device__ __forceinline__ int clamp_len(int n, int max_blocks) {
-  return max(0, min(n, max_blocks * kBlockSize));
+__device__ __forceinline__ int clamp_len(int n, int max_blocks, int block_size) {
+  return (int)max((int64_t)0, min((int64_t)n, (int64_t)max_blocks * block_size));
+}
+
+// Byte offset in a cache of token `pos` of a sequence: physical block through
+// the table, then the offset inside it. A broken entry (precondition
+// violated) reads block 0: the result is then meaningless, but the access
+// stays inside the pool.
+__device__ __forceinline__ int64_t token_offset(const DecodeArgs& a, const int32_t* bt, int pos,
+                                                int64_t row_bytes) {
+  int blk = bt[pos >> a.block_shift];
+  blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
+  return (((int64_t)blk << a.block_shift) + (pos & (a.block_size - 1))) * row_bytes;
 }
 
 #ifndef PA_DECODE_UNROLL
 #define PA_DECODE_UNROLL 8
 #endif
+
+// Load instructions per chunk. With 8 q-heads per kv-head the scores and
+// accumulators of 8 loads no longer fit the register file next to two load
+// buffers, so that group size takes chunks of 4.
+constexpr int unroll_for(int G) { return G >= 8 ? 4 : PA_DECODE_UNROLL; }
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1
 #endif
@@ -146,33 +166,28 @@ struct SplitState {
   float m[G], l[G], acc[G][8];  // running max (log2 units), sum, unnormalised output
 };
 
-// Loads of one chunk. A full chunk reads tokens c .. c+CHUNK-1 from a
-// wave-uniform base plus one per-lane offset; the tail chunk clamps every
-// token index to the last valid one (masked later), so no address ever
-// leaves the sequence's blocks.
-template <int D, int U, bool TAIL>
+// Loads of a full chunk inside one block: tokens c .. c+CHUNK-1 from a
+// wave-uniform base plus one per-lane offset.
+template <int D, int U>
 __device__ __forceinline__ void issue_chunk(const char* kbase, const char* vbase, int64_t row_bytes,
-                                            int lane_off, int row, int last, uint4 (&kr)[U],
-                                            uint4 (&vr)[U]) {
+                                            int lane_off, uint4 (&kr)[U], uint4 (&vr)[U]) {
   using S = Lanes<D>;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if constexpr (TAIL) {
-      const int t = min(u * S::TPI + row, last);
-      kr[u] = load16(kbase + t * row_bytes + lane_off);
-    } else {
-      kr[u] = load16(kbase + (int64_t)u * S::TPI * row_bytes + lane_off);
-    }
-  }
+  for (int u = 0; u < U; ++u) kr[u] = load16(kbase + (int64_t)u * S::TPI * row_bytes + lane_off);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if constexpr (TAIL) {
-      const int t = min(u * S::TPI + row, last);
-      vr[u] = load16(vbase + t * row_bytes + lane_off);
-    } else {
-      vr[u] = load16(vbase + (int64_t)u * S::TPI * row_bytes + lane_off);
-    }
-  }
+  for (int u = 0; u < U; ++u) vr[u] = load16(vbase + (int64_t)u * S::TPI * row_bytes + lane_off);
+}
+
+// Loads of a full chunk whose load groups (TPI tokens each) may lie in
+// different blocks: one base offset per group.
+template <int D, int U>
+__device__ __forceinline__ void issue_chunk_groups(const char* kc, const char* vc,
+                                                   const int64_t (&off)[U], int lane_off,
+                                                   uint4 (&kr)[U], uint4 (&vr)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) kr[u] = load16(kc + off[u] + lane_off);
+#pragma unroll
+  for (int u = 0; u < U; ++u) vr[u] = load16(vc + off[u] + lane_off);
 }
 
 template <int D, int G, int U, bool TAIL>
@@ -254,14 +269,17 @@ __device__ __forceinline__ void compute_chunk(SplitState<D, G>& st, float scale_
   }
 }
 
-template <int D, int G, bool FUSED>
+// SMALL: blocks hold fewer tokens than a chunk, so each load group looks up
+// its own block; otherwise a chunk lies inside one block.
+template <int D, int G, bool FUSED, bool SMALL>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
 void decode_split_kernel(DecodeArgs a) {
-  constexpr int U = PA_DECODE_UNROLL;
+  constexpr int U = unroll_for(G);
   using S = SplitState<D, G>;
   constexpr int LPT = Lanes<D>::LPT;
-  constexpr int CHUNK = Lanes<D>::TPI * U;  // tokens per chunk
-  static_assert(kBlockSize % CHUNK == 0, "a chunk never straddles a block");
+  constexpr int TPI = Lanes<D>::TPI;
+  constexpr int CHUNK = TPI * U;  // tokens per chunk
+  static_assert(kMinBlockSize % TPI == 0, "a load group never straddles a block");
 
   const int H_kv = a.num_kv_heads;
   const int H_q = H_kv * G;
@@ -277,7 +295,7 @@ void decode_split_kernel(DecodeArgs a) {
   const int sub = lane % LPT;  // which 8 elements of the head vector
   const int row = lane / LPT;  // which token of a load instruction
 
-  const int n = clamp_len(seq_len(a, b), a.max_blocks);
+  const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
   const int nparts = min((n + a.part_tokens - 1) / a.part_tokens, a.max_parts);
   const int64_t head0 = (int64_t)b * H_q + (int64_t)g * G;  // first q-head of the group
 
@@ -314,32 +332,35 @@ void decode_split_kernel(DecodeArgs a) {
   // k_new/v_new instead of the cache; only [start, cend) is read from the cache.
   const int cend = (FUSED && end == n) ? n - 1 : end;
   const int nfull = (cend - start) / CHUNK;  // chunks with no token past cend
-  // Byte offset of full chunk i. A broken table entry (precondition
-  // violated) is read as block 0: the result is then meaningless but every
-  // access stays inside the pool.
-  auto chunk_off = [&](int i) -> int64_t {
+  // Loads of full chunk i: one table lookup when the chunk lies in one
+  // block, else one per load group of TPI tokens.
+  auto issue = [&](int i, uint4 (&kr)[U], uint4 (&vr)[U]) {
     const int cc = start + i * CHUNK;
-    int blk = bt[cc / kBlockSize];
-    blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
-    return ((int64_t)blk * kBlockSize + (cc % kBlockSize)) * row_bytes;
+    if constexpr (!SMALL) {
+      const int64_t off = token_offset(a, bt, cc, row_bytes);
+      issue_chunk<D, U>(kc + off, vc + off, row_bytes, lane_off, kr, vr);
+    } else {
+      int64_t off[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) off[u] = token_offset(a, bt, cc + u * TPI, row_bytes);
+      issue_chunk_groups<D, U>(kc, vc, off, lane_off, kr, vr);
+    }
   };
 #if PA_DECODE_PIPE
   // Software pipeline over two register buffers: chunk i+1's loads are in
-  // flight while chunk i is multiplied. The loop body has no branches and the
-  // prefetch index is clamped, so the same number of loads is outstanding on
-  // every path and the compiler's memory-counter waits stay partial.
+  // flight while chunk i is multiplied. The loop body has no branches and
+  // the prefetch index is clamped, so the same number of loads is
+  // outstanding on every path and the compiler's memory-counter waits stay
+  // partial.
   if (nfull > 0) {
     uint4 ka[U], va[U], kb[U], vb[U];
-    int64_t off = chunk_off(0);
-    issue_chunk<D, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, ka, va);
+    issue(0, ka, va);
     int i = 0;
     for (; i + 2 <= nfull; i += 2) {
-      off = chunk_off(i + 1);
-      issue_chunk<D, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, kb, vb);
+      issue(i + 1, kb, vb);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the multiply
       compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
-      off = chunk_off(min(i + 2, nfull - 1));
-      issue_chunk<D, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, ka, va);
+      issue(min(i + 2, nfull - 1), ka, va);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
     }
@@ -347,22 +368,24 @@ void decode_split_kernel(DecodeArgs a) {
   }
 #else
   for (int i = 0; i < nfull; ++i) {
-    const int64_t off = chunk_off(i);
     uint4 kr[U], vr[U];
-    issue_chunk<D, U, false>(kc + off, vc + off, row_bytes, lane_off, row, 0, kr, vr);
+    issue(i, kr, vr);
     compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, kr, vr);
   }
 #endif
   const int c = start + nfull * CHUNK;
   if (c < cend) {
-    const int blk = bt[c / kBlockSize];
-    if (blk >= 0 && blk < a.num_blocks) {
-      const int64_t off = ((int64_t)blk * kBlockSize + (c % kBlockSize)) * row_bytes;
-      uint4 kr[U], vr[U];
-      issue_chunk<D, U, true>(kc + off, vc + off, row_bytes, tail_lane_off, row, cend - 1 - c,
-                                 kr, vr);
-      compute_chunk<D, G, U, true>(st, a.scale_log2, row, cend - c, kr, vr);
+    // tail: every lane finds its own token's row (clamped to the last valid
+    // token, which is masked out again in compute_chunk)
+    uint4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = min(u * TPI + row, cend - 1 - c);
+      const int64_t off = token_offset(a, bt, c + t, row_bytes) + tail_lane_off;
+      kr[u] = load16(kc + off);
+      vr[u] = load16(vc + off);
     }
+    compute_chunk<D, G, U, true>(st, a.scale_log2, row, cend - c, kr, vr);
   }
   if (FUSED && end == n) {
     // the newest token: attend to it from registers and write it to its slot
@@ -373,7 +396,7 @@ void decode_split_kernel(DecodeArgs a) {
     const uint4 vr1[1] = {vt};
     compute_chunk<D, G, 1, true>(st, a.scale_log2, row, 1, kr1, vr1);
     const int slot = a.slot_mapping[b];
-    if (row == 0 && slot >= 0 && slot < a.num_blocks * kBlockSize) {
+    if (row == 0 && slot >= 0 && slot < (a.num_blocks << a.block_shift)) {
       const int64_t dst = (int64_t)slot * H_kv * D + g * D + sub * 8;
       *reinterpret_cast<uint4*>(a.k_cache_w + dst) = kt;
       *reinterpret_cast<uint4*>(a.v_cache_w + dst) = vt;
@@ -435,7 +458,7 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a, int 
   constexpr int EPL = D / kWave;  // output elements per lane
   const int h = blockIdx.x % H_q;
   const int b = blockIdx.x / H_q;
-  const int n = clamp_len(seq_len(a, b), a.max_blocks);
+  const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
   const int nparts = min((n + a.part_tokens - 1) / a.part_tokens, a.max_parts);
   if (nparts <= 1) return;
   const int64_t w0 = ((int64_t)b * H_q + h) * a.max_parts;
@@ -465,16 +488,25 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a, int 
 
 using SplitFn = void (*)(DecodeArgs);
 
-template <int D, bool FUSED>
+template <int D, bool FUSED, bool SMALL>
 SplitFn pick_split(int G) {
   switch (G) {
-    case 1: return decode_split_kernel<D, 1, FUSED>;
-    case 2: return decode_split_kernel<D, 2, FUSED>;
-    case 4: return decode_split_kernel<D, 4, FUSED>;
-    case 8: return decode_split_kernel<D, 8, FUSED>;
+    case 1: return decode_split_kernel<D, 1, FUSED, SMALL>;
+    case 2: return decode_split_kernel<D, 2, FUSED, SMALL>;
+    case 4: return decode_split_kernel<D, 4, FUSED, SMALL>;
+    case 8: return decode_split_kernel<D, 8, FUSED, SMALL>;
   }
   return nullptr;
 }
+
+template <int D>
+SplitFn pick_split(int G, bool fused, bool small) {
+  if (fused) return small ? pick_split<D, true, true>(G) : pick_split<D, true, false>(G);
+  return small ? pick_split<D, false, true>(G) : pick_split<D, false, false>(G);
+}
+
+// Partition lengths are counted in units of 256 tokens, whatever the block size.
+constexpr int kPartUnit = 256;
 
 // Resident work items the split kernel keeps on an MI355X: 256 CUs x 8 waves.
 // A fixed constant (not a device query) so the workspace size is a pure
@@ -488,7 +520,7 @@ constexpr int64_t kResidentItems = 256 * 8;
 int default_partition_blocks(const pa_desc* d, int32_t num_seqs, int32_t max_ctx) {
   const int64_t mean_ctx = max(1, max_ctx / 2);
   for (int p = 8; p > 1; p >>= 1) {
-    const int64_t per_seq = (mean_ctx + (int64_t)p * kBlockSize - 1) / ((int64_t)p * kBlockSize);
+    const int64_t per_seq = (mean_ctx + (int64_t)p * kPartUnit - 1) / ((int64_t)p * kPartUnit);
     if ((int64_t)num_seqs * d->num_kv_heads * per_seq >= kResidentItems / 2) return p;
   }
   return 1;
@@ -503,7 +535,7 @@ struct Plan {
 Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part_blocks) {
   if (part_blocks <= 0) part_blocks = default_partition_blocks(d, num_seqs, max_ctx);
   Plan p;
-  p.part_tokens = part_blocks * kBlockSize;
+  p.part_tokens = part_blocks * kPartUnit;
   p.max_parts = max(1, (max_ctx + p.part_tokens - 1) / p.part_tokens);
   p.ws_bytes = p.max_parts <= 1 ? 0
                                 : (size_t)num_seqs * d->num_q_heads * p.max_parts *
@@ -527,7 +559,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !(context_lens || cu_k) || !out)
     return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", who);
-  if ((int64_t)max_blocks_per_seq * kBlockSize < max_context_len)
+  if ((int64_t)max_blocks_per_seq * desc->block_size < max_context_len)
     return fail(PA_ERR_INVALID_ARG, "%s: max_context_len %d exceeds %d table entries", who,
                 max_context_len, max_blocks_per_seq);
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15u)
@@ -578,11 +610,15 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.num_kv_heads = desc->num_kv_heads;
   a.part_tokens = plan.part_tokens;
   a.max_parts = plan.max_parts;
+  a.block_size = desc->block_size;
+  a.block_shift = log2_int(desc->block_size);
   a.scale_log2 = scale * kLog2e;
 
   hipStream_t s = (hipStream_t)stream;
-  SplitFn split = nt ? (D == 128 ? pick_split<128, true>(G) : pick_split<64, true>(G))
-                     : (D == 128 ? pick_split<128, false>(G) : pick_split<64, false>(G));
+  const int chunk = (kWave / (D / 8)) * unroll_for(G);  // tokens per chunk
+  const bool small = desc->block_size < chunk;
+  SplitFn split = D == 128 ? pick_split<128>(G, nt != nullptr, small)
+                           : pick_split<64>(G, nt != nullptr, small);
   hipLaunchKernelGGL(split, dim3((unsigned)items), dim3(kWave), 0, s, a);
   rc = launch_status(who);
   if (rc) return rc;

@@ -74,6 +74,8 @@ struct PrefillArgs {
   int32_t num_seqs;
   int32_t num_kv_heads;
   int32_t max_rblocks;  // position blocks of the longest sequence
+  int32_t block_size;   // tokens per physical block (power of two)
+  int32_t block_shift;  // log2(block_size)
   float scale_log2;
 };
 
@@ -116,34 +118,52 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-template <int D>
+// Row offset (in elements) of key position p of a sequence in a cache. A
+// broken table entry (precondition violated) reads block 0: the result is
+// then meaningless, but the access stays inside the pool.
+__device__ __forceinline__ int64_t key_row(const PrefillArgs& a, const int32_t* bt, int p,
+                                           int64_t row_elems) {
+  const int blk_raw = bt[p >> a.block_shift];
+  const int64_t blk = (blk_raw >= 0 && blk_raw < a.num_blocks) ? blk_raw : 0;
+  return ((blk << a.block_shift) + (p & (a.block_size - 1))) * row_elems;
+}
+
+// Register loads of stage `stage` (keys [64*stage, 64*stage + 64)). Keys at
+// or past kmax are never visible; they re-read the last needed one. SMALL:
+// blocks hold fewer keys than a stage, so every key looks up its own block;
+// otherwise the whole stage lies in one block (one lookup).
+template <int D, bool SMALL>
 __device__ __forceinline__ void load_stage(const PrefillArgs& a, const int32_t* bt, int g, int kmax,
                                            int stage, u32x4 (&kreg)[Geo<D>::KCHUNKS],
                                            typename VVec<Geo<D>::VW>::T (&vreg)[2]) {
   using GG = Geo<D>;
   const int t = threadIdx.x;
   const int kbase = stage * kKT;
-  const int blk_raw = bt[kbase / kBlockSize];
-  const int64_t blk = (blk_raw >= 0 && blk_raw < a.num_blocks) ? blk_raw : 0;
   const int64_t row_elems = (int64_t)a.num_kv_heads * D;
-  // keys at or past kmax are never visible; re-read the last needed one
-  const uint16_t* kb = a.k_cache + (blk * kBlockSize) * row_elems + (int64_t)g * D;
-  const uint16_t* vb = a.v_cache + (blk * kBlockSize) * row_elems + (int64_t)g * D;
+  const uint16_t* kc = a.k_cache + (int64_t)g * D;
+  const uint16_t* vc = a.v_cache + (int64_t)g * D;
+  int64_t base = 0;
+  if constexpr (!SMALL) base = key_row(a, bt, kbase, row_elems) - (int64_t)kbase * row_elems;
+  // row offset of key position p (base + p rows when the stage is in one block)
+  auto row_of = [&](int p) -> int64_t {
+    if constexpr (SMALL) return key_row(a, bt, p, row_elems);
+    else return base + (int64_t)p * row_elems;
+  };
 #pragma unroll
   for (int i = 0; i < GG::KCHUNKS; ++i) {
     const int c = t + i * kThreads;
     const int key = c / (D / 8);
     const int ch = c % (D / 8);
-    const int kp = min(kbase + key, kmax - 1) % kBlockSize;
-    kreg[i] = *reinterpret_cast<const u32x4*>(kb + kp * row_elems + ch * 8);
+    const int kp = min(kbase + key, kmax - 1);
+    kreg[i] = *reinterpret_cast<const u32x4*>(kc + row_of(kp) + ch * 8);
   }
   typedef typename VVec<GG::VW>::T VT;
   const int pair = t % 32;  // keys 2*pair, 2*pair+1 of the stage
   const int dg = t / 32;    // d range [dg*VW, dg*VW+VW)
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int kp = min(kbase + 2 * pair + s, kmax - 1) % kBlockSize;
-    vreg[s] = *reinterpret_cast<const VT*>(vb + kp * row_elems + dg * GG::VW);
+    const int kp = min(kbase + 2 * pair + s, kmax - 1);
+    vreg[s] = *reinterpret_cast<const VT*>(vc + row_of(kp) + dg * GG::VW);
   }
 }
 
@@ -177,7 +197,7 @@ __device__ __forceinline__ void store_stage(char* lds, const u32x4 (&kreg)[Geo<D
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool SMALL>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   using GG = Geo<D>;
   constexpr int QB = kCols / G;              // query positions per workgroup
@@ -207,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int q0 = a.cu_q[b];
   const int q_len = a.cu_q[b + 1] - q0;
   int k_len = a.cu_k[b + 1] - a.cu_k[b];
-  k_len = min(k_len, a.max_blocks * kBlockSize);
+  k_len = (int)min((int64_t)k_len, (int64_t)a.max_blocks * a.block_size);
   if (q_len <= 0 || k_len < q_len) return;  // nothing to do / broken precondition
   const int p_end = q_len - r * QB;         // positions [p_end - QB, p_end)
   if (p_end <= 0) return;
@@ -261,9 +281,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   // counter waits stay static.
   u32x4 kra[GG::KCHUNKS], krb[GG::KCHUNKS];
   typename VVec<GG::VW>::T vra[2], vrb[2];
-  load_stage<D>(a, bt, g, kmax, 0, kra, vra);
+  load_stage<D, SMALL>(a, bt, g, kmax, 0, kra, vra);
   store_stage<D>(lds, kra, vra);
-  load_stage<D>(a, bt, g, kmax, min(1, n_stages - 1), kra, vra);
+  load_stage<D, SMALL>(a, bt, g, kmax, min(1, n_stages - 1), kra, vra);
   __syncthreads();
 
   // One stage: issue the loads of stage st+2 into `next`, multiply the LDS
@@ -271,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   auto stage_step = [&](int st, const u32x4 (&kready)[GG::KCHUNKS],
                         const typename VVec<GG::VW>::T (&vready)[2], u32x4 (&knext)[GG::KCHUNKS],
                         typename VVec<GG::VW>::T (&vnext)[2]) {
-    load_stage<D>(a, bt, g, kmax, min(st + 2, n_stages - 1), knext, vnext);
+    load_stage<D, SMALL>(a, bt, g, kmax, min(st + 2, n_stages - 1), knext, vnext);
     const char* ks_lds = lds + (st & 1) * GG::STAGE;
     const char* vt_lds = ks_lds + GG::KBYTES;
     const int key0 = st * kKT;  // absolute position of the stage's first key
@@ -395,13 +415,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
 using PrefillFn = void (*)(PrefillArgs);
 
-template <int D>
+template <int D, bool SMALL>
 PrefillFn pick(int G) {
   switch (G) {
-    case 1: return prefill_kernel<D, 1>;
-    case 2: return prefill_kernel<D, 2>;
-    case 4: return prefill_kernel<D, 4>;
-    case 8: return prefill_kernel<D, 8>;
+    case 1: return prefill_kernel<D, 1, SMALL>;
+    case 2: return prefill_kernel<D, 2, SMALL>;
+    case 4: return prefill_kernel<D, 4, SMALL>;
+    case 8: return prefill_kernel<D, 8, SMALL>;
   }
   return nullptr;
 }
@@ -427,7 +447,7 @@ int launch_prefill(const char* who, const void* q, const void* k_cache, const vo
   if (max_seqlen_q > max_seqlen_k)
     return fail(PA_ERR_INVALID_ARG, "%s: max_seqlen_q %d > max_seqlen_k %d", who, max_seqlen_q,
                 max_seqlen_k);
-  if ((int64_t)max_blocks_per_seq * kBlockSize < max_seqlen_k)
+  if ((int64_t)max_blocks_per_seq * desc->block_size < max_seqlen_k)
     return fail(PA_ERR_INVALID_ARG, "%s: max_seqlen_k %d exceeds %d table entries", who,
                 max_seqlen_k, max_blocks_per_seq);
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15u)
@@ -452,8 +472,12 @@ int launch_prefill(const char* who, const void* q, const void* k_cache, const vo
   a.num_seqs = num_seqs;
   a.num_kv_heads = desc->num_kv_heads;
   a.max_rblocks = (int32_t)rblocks;
+  a.block_size = desc->block_size;
+  a.block_shift = log2_int(desc->block_size);
   a.scale_log2 = scale * kLog2e;
-  PrefillFn fn = D == 128 ? pick<128>(G) : pick<64>(G);
+  const bool small = desc->block_size < kKT;
+  PrefillFn fn = D == 128 ? (small ? pick<128, true>(G) : pick<128, false>(G))
+                          : (small ? pick<64, true>(G) : pick<64, false>(G));
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a);
   return launch_status(who);
 }

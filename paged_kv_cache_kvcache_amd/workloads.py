@@ -274,27 +274,30 @@ DESCRIPTIONS = {
 }
 
 
-def make_case(name: str, seed: int | None = None, threads: int | None = None):
-    """The five named workloads (lengths drawn first from the case's rng)."""
+def make_case(name: str, seed: int | None = None, threads: int | None = None,
+              block_size: int = BLOCK_SIZE):
+    """The named workloads (lengths drawn first from the case's rng). Another
+    block size keeps every length and draw; only the pool's shape, the tables
+    and (for "tiny") the pool size change."""
     seed = SEEDS[name] if seed is None else seed
+    kw = dict(name=name, threads=threads, block_size=block_size)
     if name == "tiny":
-        return decode_case(4, 2, 64, [1, 17, 256, 300], seed + 1, num_blocks=16, name=name,
-                           threads=threads)
+        return decode_case(4, 2, 64, [1, 17, 256, 300], seed + 1,
+                           num_blocks=16 if block_size == BLOCK_SIZE else None, **kw)
     if name == "qwen3-0.6b":
         ctx = np.random.default_rng(seed).integers(128, 4096 + 1, size=64)
-        return decode_case(16, 8, 128, ctx, seed + 1, name=name, threads=threads)
+        return decode_case(16, 8, 128, ctx, seed + 1, **kw)
     if name == "qwen3-8b":
         ctx = np.random.default_rng(seed).integers(512, 8192 + 1, size=256)
-        return decode_case(32, 8, 128, ctx, seed + 1, name=name, threads=threads)
+        return decode_case(32, 8, 128, ctx, seed + 1, **kw)
     if name == "long":
-        return decode_case(32, 8, 128, [16384] * 32, seed + 1, name=name, threads=threads)
+        return decode_case(32, 8, 128, [16384] * 32, seed + 1, **kw)
     if name == "prefill":
         suffix = np.random.default_rng(seed).integers(100, 2000 + 1, size=16)
-        return prefill_case(32, 8, 128, 1024, suffix, seed + 1, name=name, threads=threads)
+        return prefill_case(32, 8, 128, 1024, suffix, seed + 1, **kw)
     if name == "mixed":
         rng = np.random.default_rng(seed)
         dec = rng.integers(512, 8192 + 1, size=224)
         cached = rng.integers(100, 4000 + 1, size=4)
-        return mixed_case(32, 8, 128, dec, [(int(c), 512) for c in cached], seed + 1,
-                          name=name, threads=threads)
+        return mixed_case(32, 8, 128, dec, [(int(c), 512) for c in cached], seed + 1, **kw)
     raise KeyError(name)

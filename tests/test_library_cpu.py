@@ -58,9 +58,12 @@ def test_host_argument_checks_need_no_gpu(lib):
     assert lib.pa_decode(None, None, None, None, 0, None, 1, 0, 1.0, None, None, 0,
                          ctypes.byref(bad), None) == B.PA_ERR_INVALID_ARG
     assert b"multiple" in lib.pa_last_error()
-    for kw in (dict(d=96), dict(bsz=16), dict(h_q=24, h_kv=2)):
+    for kw in (dict(d=96), dict(bsz=8), dict(bsz=48), dict(bsz=2048), dict(h_q=24, h_kv=2)):
         assert lib.pa_decode(None, None, None, None, 0, None, 1, 0, 1.0, None, None, 0,
                              ctypes.byref(_desc(**kw)), None) == B.PA_ERR_UNSUPPORTED
+    for bsz in (16, 32, 64, 128, 512, 1024):  # every built block size: an empty batch is a no-op
+        assert lib.pa_decode(None, None, None, None, 0, None, 0, 0, 1.0, None, None, 0,
+                             ctypes.byref(_desc(bsz=bsz)), None) == 0
     assert lib.pa_decode(None, None, None, None, 0, None, 0, 0, 1.0, None, None, 0,
                          ctypes.byref(d), None) == 0  # empty batch: no-op
     # workspace checked before any launch
