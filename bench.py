@@ -30,7 +30,9 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 LAYERS_QWEN3_8B = 36
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_decode_qwen3-8b.json")
+PMC_PREFILL_FILE = os.path.join(ROOT, "profiles", "pmc_prefill_prefix1024.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_kvcache_amd", "csrc", "decode.hip")
+PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_kvcache_amd", "csrc", "prefill.hip")
 
 
 def decode_bytes(case) -> int:
@@ -65,17 +67,18 @@ def src_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_src: str, mode: str, block_size: int = 256):
-    """HBM bytes per launch of the dominant call from the committed rocprofv3
-    counter summary, or None if it is missing, was taken for another step
-    mode or block size, or on a different kernel source."""
+def traffic_from_profile(pmc_file: str, kernel_src: str, mode: str | None,
+                         block_size: int = 256):
+    """HBM bytes per launch of a call from a committed rocprofv3 counter
+    summary, or None if it is missing, was taken for another step mode or
+    block size, or on a different kernel source."""
     try:
-        with open(PMC_FILE) as f:
+        with open(pmc_file) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     if (rec.get("source_sha256_16") != src_hash(kernel_src) or rec.get("step_mode") != mode
-            or rec.get("block_size", 256) != block_size):
+            or rec.get("block_size") != block_size):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -158,7 +161,7 @@ def run_prefill(args, torch, B, W, dev):
         "roofline": {"bound": "mfma", "achieved": round(flops / t_attn / 1e12, 2),
                      "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(flops / t_attn / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic_from_profile(PMC_PREFILL_FILE, PREFILL_SRC, None)},
         "q_tokens_per_s": round(int(qlens.sum()) / (t_store + t_attn), 1),
     }
 
@@ -360,7 +363,7 @@ def main() -> int:
         dom, dom_bytes = "pa_decode", db
         dom_desc = "pa_decode (split-K + merge)"
     dom_gbs = dom_bytes / (ms_call[dom] * 1e-3) / 1e9
-    traffic = traffic_from_profile(DECODE_SRC, args.mode, args.block_size)
+    traffic = traffic_from_profile(PMC_FILE, DECODE_SRC, args.mode, args.block_size)
 
     rec = {
         "metric": "paged decode: KV GB/s (% HBM peak) + tokens/s at Qwen3-8B shape, batch 256",
