@@ -348,23 +348,34 @@ void decode_split_kernel(DecodeArgs a) {
   };
 #if PA_DECODE_PIPE
   // Software pipeline over two register buffers: chunk i+1's loads are in
-  // flight while chunk i is multiplied. The loop body has no branches and
-  // the prefetch index is clamped, so the same number of loads is
-  // outstanding on every path and the compiler's memory-counter waits stay
-  // partial.
+  // flight while chunk i is multiplied. The loop body has no branches, so
+  // the same number of loads is outstanding on every path and the
+  // compiler's memory-counter waits stay partial. The last one or two
+  // chunks are finished after the loop, so no chunk is loaded twice; with
+  // 8 q-heads that epilogue no longer fits the register file, and the loop
+  // instead runs to the end with the prefetch index clamped (the last chunk
+  // is then loaded twice).
   if (nfull > 0) {
+    constexpr bool kEpilogue = G < 8;
     uint4 ka[U], va[U], kb[U], vb[U];
     issue(0, ka, va);
     int i = 0;
-    for (; i + 2 <= nfull; i += 2) {
+    for (; kEpilogue ? i + 2 < nfull : i + 2 <= nfull; i += 2) {
       issue(i + 1, kb, vb);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the multiply
       compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
-      issue(min(i + 2, nfull - 1), ka, va);
+      issue(kEpilogue ? i + 2 : min(i + 2, nfull - 1), ka, va);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
     }
-    if (i < nfull) compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
+    if (kEpilogue && i + 1 < nfull) {
+      issue(i + 1, kb, vb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
+      compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
+    } else if (i < nfull) {
+      compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
+    }
   }
 #else
   for (int i = 0; i < nfull; ++i) {
@@ -513,7 +524,7 @@ constexpr int kPartUnit = 256;
 // function of the arguments.
 constexpr int64_t kResidentItems = 256 * 8;
 
-// Longest partition (8, 4, 2 or 1 blocks) whose item count still fills half
+// Longest partition (8, 4, 2 or 1 units of 256 tokens) whose item count still fills half
 // the resident slots, estimating the mean context as max_context_len / 2.
 // Long partitions amortise each item's set-up and keep its loads streaming;
 // short ones keep small batches spread over the whole chip.
