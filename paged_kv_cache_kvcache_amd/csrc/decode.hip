@@ -269,6 +269,92 @@ __device__ __forceinline__ void compute_chunk(SplitState<D, G>& st, float scale_
   }
 }
 
+#ifndef PA_DECODE_ORDER
+#define PA_DECODE_ORDER 1
+#endif
+
+// Dispatch order of the split kernel's work items, longest first. The
+// kernel is bandwidth-bound and its items differ in length (a sequence's
+// last partition is partial), so handing out the longest items first lets
+// the grid drain on short ones instead of ending on a few long stragglers.
+// Items are ranked by length bucket (32 buckets of part_tokens/32 tokens,
+// full partitions in the top one; empty sequences, which only write zeros,
+// last), then by (sequence, partition). Every wave derives its own item
+// from the sequence lengths (a pass over them for the bucket histogram, a
+// second one to locate its rank inside the bucket), so no ordering kernel
+// or buffer is needed.
+constexpr int kOrderBuckets = 32;
+
+__device__ __forceinline__ int len_bucket(int len, int part_tokens) {
+  return 1 + (int)(((int64_t)(len - 1) * kOrderBuckets) / part_tokens);  // 1..32
+}
+
+// Items of sequence length n in bucket k (n already clamped to max_parts
+// partitions): full partitions sit in the top bucket, the partial last one
+// in its length's bucket, an empty sequence in bucket 0.
+__device__ __forceinline__ int items_in_bucket(int n, int k, int part_tokens) {
+  if (n == 0) return k == 0;
+  const int f = n / part_tokens, rem = n % part_tokens;
+  return (k == kOrderBuckets ? f : 0) + (rem > 0 && len_bucket(rem, part_tokens) == k);
+}
+
+// Finds the (sequence, partition) of rank r; false when r is past the last item.
+__device__ bool find_item(const DecodeArgs& a, int r, int& seq, int& part) {
+  __shared__ int hist[kOrderBuckets + 1];
+  const int lane = threadIdx.x;
+  const int P = a.part_tokens;
+  const int cap = a.max_parts * P;  // a length beyond max_context_len is cut here
+  if (lane <= kOrderBuckets) hist[lane] = 0;
+  __syncthreads();
+  for (int s = lane; s < a.num_seqs; s += kWave) {
+    const int n = min(clamp_len(seq_len(a, s), a.max_blocks, a.block_size), cap);
+    if (n == 0) {
+      atomicAdd(&hist[0], 1);
+    } else {
+      if (n / P) atomicAdd(&hist[kOrderBuckets], n / P);
+      if (n % P) atomicAdd(&hist[len_bucket(n % P, P)], 1);
+    }
+  }
+  __syncthreads();
+  int k = kOrderBuckets;
+  for (; k >= 0; --k) {
+    const int c = hist[k];
+    if (r < c) break;
+    r -= c;
+  }
+  if (k < 0) return false;
+  // the r-th item of bucket k in (sequence, partition) order
+  for (int base = 0; base < a.num_seqs; base += kWave) {
+    const int s = base + lane;
+    const int n = s < a.num_seqs ? min(clamp_len(seq_len(a, s), a.max_blocks, a.block_size), cap)
+                                 : 0;
+    const int c = s < a.num_seqs ? items_in_bucket(n, k, P) : 0;
+    int incl = c;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += t;
+    }
+    const int total = __shfl(incl, kWave - 1, kWave);
+    if (r < total) {
+      const uint64_t hit = __ballot(incl > r);
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      const int before = __shfl(incl - c, L, kWave);
+      const int nl = __shfl(n, L, kWave);
+      const int within = r - before;
+      // top bucket: the full partitions 0..f-1 first, then a partial one
+      const int pt = (k == kOrderBuckets && within < nl / P) ? within : (k == 0 ? 0 : nl / P);
+      // both are wave-uniform: say so, so everything derived from them
+      // (lengths, table row, chunk bases) stays in scalar registers
+      seq = __builtin_amdgcn_readfirstlane(base + L);
+      part = __builtin_amdgcn_readfirstlane(pt);
+      return true;
+    }
+    r -= total;
+  }
+  return false;  // not reached: the histogram counted this item
+}
+
 // SMALL: blocks hold fewer tokens than a chunk, so each load group looks up
 // its own block; otherwise a chunk lies inside one block.
 template <int D, int G, bool FUSED, bool SMALL>
@@ -283,14 +369,20 @@ void decode_split_kernel(DecodeArgs a) {
 
   const int H_kv = a.num_kv_heads;
   const int H_q = H_kv * G;
-  // Items are dispatched highest partition first: the grid then drains on the
-  // first partitions, which every sequence has, instead of on the tails of
-  // a few long sequences.
+#if PA_DECODE_ORDER
+  // items longest first (find_item); the kv-heads of one item are adjacent
+  const int g = blockIdx.x % H_kv;
+  int b, part;
+  if (!find_item(a, blockIdx.x / H_kv, b, part)) return;
+  __builtin_amdgcn_sched_barrier(0);  // keep the item search apart from the main loop
+#else
+  // highest partition first
   int idx = blockIdx.x;
   const int g = idx % H_kv;
   idx /= H_kv;
   const int b = idx % a.num_seqs;
   const int part = a.max_parts - 1 - idx / a.num_seqs;
+#endif
   const int lane = threadIdx.x;
   const int sub = lane % LPT;  // which 8 elements of the head vector
   const int row = lane / LPT;  // which token of a load instruction
