@@ -151,12 +151,15 @@ __device__ __forceinline__ uint32_t pack2_bf16_hw(float lo, float hi) {
 // range flush to zero, which is what a softmax weight that small should be.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Lane geometry: d/8 lanes hold one token's head vector (16 bytes each), so a
-// wave load instruction covers TPI tokens.
-template <int D>
+// Lane geometry: d/8 lanes hold one kv-head's vector of a token (16 bytes
+// each); KPW adjacent kv-heads of the same token form one contiguous segment
+// of KPW * 2d bytes, and a wave load instruction covers TPI tokens of it.
+template <int D, int KPW>
 struct Lanes {
-  static constexpr int LPT = D / 8;        // lanes per token vector
-  static constexpr int TPI = kWave / LPT;  // tokens per wave load instruction
+  static constexpr int LPT = D / 8;             // lanes per kv-head vector
+  static constexpr int SEG = LPT * KPW;         // lanes per token segment
+  static constexpr int TPI = kWave / SEG;       // tokens per wave load instruction
+  static_assert(kWave % SEG == 0, "segments tile the wave");
 };
 
 // Per-wave state of one work item.
@@ -168,10 +171,9 @@ struct SplitState {
 
 // Loads of a full chunk inside one block: tokens c .. c+CHUNK-1 from a
 // wave-uniform base plus one per-lane offset.
-template <int D, int U>
+template <class S, int U>
 __device__ __forceinline__ void issue_chunk(const char* kbase, const char* vbase, int64_t row_bytes,
                                             int lane_off, uint4 (&kr)[U], uint4 (&vr)[U]) {
-  using S = Lanes<D>;
 #pragma unroll
   for (int u = 0; u < U; ++u) kr[u] = load16(kbase + (int64_t)u * S::TPI * row_bytes + lane_off);
 #pragma unroll
@@ -180,7 +182,7 @@ __device__ __forceinline__ void issue_chunk(const char* kbase, const char* vbase
 
 // Loads of a full chunk whose load groups (TPI tokens each) may lie in
 // different blocks: one base offset per group.
-template <int D, int U>
+template <int U>
 __device__ __forceinline__ void issue_chunk_groups(const char* kc, const char* vc,
                                                    const int64_t (&off)[U], int lane_off,
                                                    uint4 (&kr)[U], uint4 (&vr)[U]) {
@@ -190,11 +192,10 @@ __device__ __forceinline__ void issue_chunk_groups(const char* kc, const char* v
   for (int u = 0; u < U; ++u) vr[u] = load16(vc + off[u] + lane_off);
 }
 
-template <int D, int G, int U, bool TAIL>
+template <class S, int D, int G, int U, bool TAIL>
 __device__ __forceinline__ void compute_chunk(SplitState<D, G>& st, float scale_log2, int row,
                                               int nvalid, const uint4 (&kr)[U],
                                               const uint4 (&vr)[U]) {
-  using S = Lanes<D>;
   float s[U][G];  // raw q.k (unscaled)
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -355,37 +356,42 @@ __device__ bool find_item(const DecodeArgs& a, int r, int& seq, int& part) {
   return false;  // not reached: the histogram counted this item
 }
 
+// A work item is (sequence, group of KPW adjacent kv-heads, partition).
 // SMALL: blocks hold fewer tokens than a chunk, so each load group looks up
 // its own block; otherwise a chunk lies inside one block.
-template <int D, int G, bool FUSED, bool SMALL>
+template <int D, int G, int KPW, bool FUSED, bool SMALL>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
 void decode_split_kernel(DecodeArgs a) {
   constexpr int U = unroll_for(G);
   using S = SplitState<D, G>;
-  constexpr int LPT = Lanes<D>::LPT;
-  constexpr int TPI = Lanes<D>::TPI;
+  using L = Lanes<D, KPW>;
+  constexpr int LPT = L::LPT;
+  constexpr int SEG = L::SEG;
+  constexpr int TPI = L::TPI;
   constexpr int CHUNK = TPI * U;  // tokens per chunk
   static_assert(kMinBlockSize % TPI == 0, "a load group never straddles a block");
 
   const int H_kv = a.num_kv_heads;
   const int H_q = H_kv * G;
+  const int n_groups = H_kv / KPW;  // kv-head groups (the host checks divisibility)
 #if PA_DECODE_ORDER
-  // items longest first (find_item); the kv-heads of one item are adjacent
-  const int g = blockIdx.x % H_kv;
+  // items longest first (find_item); the kv-head groups of one item are adjacent
+  const int gw = blockIdx.x % n_groups;
   int b, part;
-  if (!find_item(a, blockIdx.x / H_kv, b, part)) return;
+  if (!find_item(a, blockIdx.x / n_groups, b, part)) return;
   __builtin_amdgcn_sched_barrier(0);  // keep the item search apart from the main loop
 #else
   // highest partition first
   int idx = blockIdx.x;
-  const int g = idx % H_kv;
-  idx /= H_kv;
+  const int gw = idx % n_groups;
+  idx /= n_groups;
   const int b = idx % a.num_seqs;
   const int part = a.max_parts - 1 - idx / a.num_seqs;
 #endif
   const int lane = threadIdx.x;
-  const int sub = lane % LPT;  // which 8 elements of the head vector
-  const int row = lane / LPT;  // which token of a load instruction
+  const int sub = lane % LPT;                 // which 8 elements of the head vector
+  const int g = gw * KPW + (lane / LPT) % KPW;  // this lane's kv-head
+  const int row = lane / SEG;                 // which token of a load instruction
 
   const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
   const int nparts = min((n + a.part_tokens - 1) / a.part_tokens, a.max_parts);
@@ -430,12 +436,12 @@ void decode_split_kernel(DecodeArgs a) {
     const int cc = start + i * CHUNK;
     if constexpr (!SMALL) {
       const int64_t off = token_offset(a, bt, cc, row_bytes);
-      issue_chunk<D, U>(kc + off, vc + off, row_bytes, lane_off, kr, vr);
+      issue_chunk<L, U>(kc + off, vc + off, row_bytes, lane_off, kr, vr);
     } else {
       int64_t off[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) off[u] = token_offset(a, bt, cc + u * TPI, row_bytes);
-      issue_chunk_groups<D, U>(kc, vc, off, lane_off, kr, vr);
+      issue_chunk_groups<U>(kc, vc, off, lane_off, kr, vr);
     }
   };
 #if PA_DECODE_PIPE
@@ -455,25 +461,25 @@ void decode_split_kernel(DecodeArgs a) {
     for (; kEpilogue ? i + 2 < nfull : i + 2 <= nfull; i += 2) {
       issue(i + 1, kb, vb);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the multiply
-      compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
+      compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
       issue(kEpilogue ? i + 2 : min(i + 2, nfull - 1), ka, va);
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
+      compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
     }
     if (kEpilogue && i + 1 < nfull) {
       issue(i + 1, kb, vb);
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
-      compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
+      compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
+      compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
     } else if (i < nfull) {
-      compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
+      compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
     }
   }
 #else
   for (int i = 0; i < nfull; ++i) {
     uint4 kr[U], vr[U];
     issue(i, kr, vr);
-    compute_chunk<D, G, U, false>(st, a.scale_log2, row, CHUNK, kr, vr);
+    compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, kr, vr);
   }
 #endif
   const int c = start + nfull * CHUNK;
@@ -488,7 +494,7 @@ void decode_split_kernel(DecodeArgs a) {
       kr[u] = load16(kc + off);
       vr[u] = load16(vc + off);
     }
-    compute_chunk<D, G, U, true>(st, a.scale_log2, row, cend - c, kr, vr);
+    compute_chunk<L, D, G, U, true>(st, a.scale_log2, row, cend - c, kr, vr);
   }
   if (FUSED && end == n) {
     // the newest token: attend to it from registers and write it to its slot
@@ -497,7 +503,7 @@ void decode_split_kernel(DecodeArgs a) {
     const uint4 vt = *reinterpret_cast<const uint4*>(a.v_new + (int64_t)b * a.v_new_stride + g * D + sub * 8);
     const uint4 kr1[1] = {kt};
     const uint4 vr1[1] = {vt};
-    compute_chunk<D, G, 1, true>(st, a.scale_log2, row, 1, kr1, vr1);
+    compute_chunk<L, D, G, 1, true>(st, a.scale_log2, row, 1, kr1, vr1);
     const int slot = a.slot_mapping[b];
     if (row == 0 && slot >= 0 && slot < (a.num_blocks << a.block_shift)) {
       const int64_t dst = (int64_t)slot * H_kv * D + g * D + sub * 8;
@@ -506,21 +512,22 @@ void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  // Merge the token-rows of lanes (each has its own running max).
+  // Merge the token-rows of lanes (each has its own running max); lanes
+  // SEG apart hold the same kv-head.
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float M = st.m[h];
 #pragma unroll
-    for (int off = LPT; off < kWave; off <<= 1) M = fmaxf(M, xor_lane(M, off));
+    for (int off = SEG; off < kWave; off <<= 1) M = fmaxf(M, xor_lane(M, off));
     const float w = (st.m[h] == -INFINITY) ? 0.f : exp2f(st.m[h] - M);
     float lh = st.l[h] * w;
 #pragma unroll
-    for (int off = LPT; off < kWave; off <<= 1) lh += xor_lane(lh, off);
+    for (int off = SEG; off < kWave; off <<= 1) lh += xor_lane(lh, off);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float o = st.acc[h][e] * w;
 #pragma unroll
-      for (int off = LPT; off < kWave; off <<= 1) o += xor_lane(o, off);
+      for (int off = SEG; off < kWave; off <<= 1) o += xor_lane(o, off);
       st.acc[h][e] = o;
     }
     st.m[h] = M;
@@ -549,7 +556,8 @@ void decode_split_kernel(DecodeArgs a) {
         dst[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
         dst[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
       }
-      if (lane == 0) *reinterpret_cast<float2*>(a.ws_ml + wi * 2) = make_float2(st.m[h], st.l[h]);
+      if (row == 0 && sub == 0)
+        *reinterpret_cast<float2*>(a.ws_ml + wi * 2) = make_float2(st.m[h], st.l[h]);
     }
   }
 }
@@ -591,21 +599,36 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a, int 
 
 using SplitFn = void (*)(DecodeArgs);
 
-template <int D, bool FUSED, bool SMALL>
+template <int D, int KPW, bool FUSED, bool SMALL>
 SplitFn pick_split(int G) {
   switch (G) {
-    case 1: return decode_split_kernel<D, 1, FUSED, SMALL>;
-    case 2: return decode_split_kernel<D, 2, FUSED, SMALL>;
-    case 4: return decode_split_kernel<D, 4, FUSED, SMALL>;
-    case 8: return decode_split_kernel<D, 8, FUSED, SMALL>;
+    case 1: return decode_split_kernel<D, 1, KPW, FUSED, SMALL>;
+    case 2: return decode_split_kernel<D, 2, KPW, FUSED, SMALL>;
+    case 4: return decode_split_kernel<D, 4, KPW, FUSED, SMALL>;
+    case 8: return decode_split_kernel<D, 8, KPW, FUSED, SMALL>;
   }
   return nullptr;
 }
 
-template <int D>
+template <int D, int KPW>
 SplitFn pick_split(int G, bool fused, bool small) {
-  if (fused) return small ? pick_split<D, true, true>(G) : pick_split<D, true, false>(G);
-  return small ? pick_split<D, false, true>(G) : pick_split<D, false, false>(G);
+  if (fused) return small ? pick_split<D, KPW, true, true>(G) : pick_split<D, KPW, true, false>(G);
+  return small ? pick_split<D, KPW, false, true>(G) : pick_split<D, KPW, false, false>(G);
+}
+
+#ifndef PA_DECODE_SEGMENT
+#define PA_DECODE_SEGMENT 512
+#endif
+
+// kv-heads per wave: as many adjacent heads as make a PA_DECODE_SEGMENT-byte
+// contiguous piece of each token row (on MI355X 512-byte pieces stream about
+// 7% faster than 256-byte ones), when the head count allows it; else one.
+// With 8 q-heads per kv-head the wave's arithmetic per byte is highest and
+// its chunks are shortest; there one kv-head per wave measures faster.
+int kv_heads_per_wave(int head_dim, int num_q_heads, int num_kv_heads) {
+  if (num_q_heads / num_kv_heads >= 8) return 1;
+  const int want = PA_DECODE_SEGMENT / (2 * head_dim);
+  return (want > 1 && num_kv_heads % want == 0) ? want : 1;
 }
 
 // Partition lengths are counted in units of 256 tokens, whatever the block size.
@@ -616,15 +639,19 @@ constexpr int kPartUnit = 256;
 // function of the arguments.
 constexpr int64_t kResidentItems = 256 * 8;
 
-// Longest partition (8, 4, 2 or 1 units of 256 tokens) whose item count still fills half
-// the resident slots, estimating the mean context as max_context_len / 2.
-// Long partitions amortise each item's set-up and keep its loads streaming;
-// short ones keep small batches spread over the whole chip.
+// Longest partition (16 (multi-head waves only), 8, 4, 2 or 1 units of 256
+// tokens) whose item count still fills half the resident slots, estimating
+// the mean context as max_context_len / 2. Long partitions amortise each
+// item's set-up and keep its loads streaming (fewer concurrent streams also
+// read HBM more efficiently); short ones keep small batches spread over the
+// whole chip.
 int default_partition_blocks(const pa_desc* d, int32_t num_seqs, int32_t max_ctx) {
   const int64_t mean_ctx = max(1, max_ctx / 2);
-  for (int p = 8; p > 1; p >>= 1) {
+  const int kpw = kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
+  const int groups = d->num_kv_heads / kpw;
+  for (int p = kpw > 1 ? 16 : 8; p > 1; p >>= 1) {
     const int64_t per_seq = (mean_ctx + (int64_t)p * kPartUnit - 1) / ((int64_t)p * kPartUnit);
-    if ((int64_t)num_seqs * d->num_kv_heads * per_seq >= kResidentItems / 2) return p;
+    if ((int64_t)num_seqs * groups * per_seq >= kResidentItems / 2) return p;
   }
   return 1;
 }
@@ -686,7 +713,8 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
     if ((uintptr_t)workspace & 15u)
       return fail(PA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", who);
   }
-  const int64_t items = (int64_t)num_seqs * desc->num_kv_heads * plan.max_parts;
+  const int kpw = kv_heads_per_wave(desc->head_dim, desc->num_q_heads, desc->num_kv_heads);
+  const int64_t items = (int64_t)num_seqs * (desc->num_kv_heads / kpw) * plan.max_parts;
   if (items > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "%s: grid too large", who);
 
   DecodeArgs a;
@@ -718,10 +746,19 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.scale_log2 = scale * kLog2e;
 
   hipStream_t s = (hipStream_t)stream;
-  const int chunk = (kWave / (D / 8)) * unroll_for(G);  // tokens per chunk
+  const int chunk = (kWave / (D / 8 * kpw)) * unroll_for(G);  // tokens per chunk
   const bool small = desc->block_size < chunk;
-  SplitFn split = D == 128 ? pick_split<128>(G, nt != nullptr, small)
-                           : pick_split<64>(G, nt != nullptr, small);
+  const bool fused = nt != nullptr;
+  SplitFn split = nullptr;
+  if (D == 128) {
+    split = kpw == 2 ? pick_split<128, 2>(G, fused, small) : pick_split<128, 1>(G, fused, small);
+  } else {
+    split = kpw == 4   ? pick_split<64, 4>(G, fused, small)
+            : kpw == 2 ? pick_split<64, 2>(G, fused, small)
+                       : pick_split<64, 1>(G, fused, small);
+  }
+  if (!split || (D == 128 && kpw > 2))
+    return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for %d kv-heads per wave", who, kpw);
   hipLaunchKernelGGL(split, dim3((unsigned)items), dim3(kWave), 0, s, a);
   rc = launch_status(who);
   if (rc) return rc;
