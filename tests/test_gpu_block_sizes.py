@@ -36,7 +36,7 @@ def _slots(case, ends):
 
 
 @pytest.mark.parametrize("bsz", BLOCK_SIZES)
-@pytest.mark.parametrize("h_q,h_kv,d", [(32, 8, 128), (8, 1, 64), (64, 8, 128)])
+@pytest.mark.parametrize("h_q,h_kv,d", [(32, 8, 128), (8, 1, 64), (64, 8, 128), (32, 8, 64)])
 def test_store_and_decode(bsz, h_q, h_kv, d):
     case = W.decode_case(h_q, h_kv, d, LENS, seed=90 + bsz + d, block_size=bsz)
     print("block size %d decode H=%d/%d d=%d pool=%d blocks" % (bsz, h_q, h_kv, d,
@@ -58,8 +58,9 @@ def test_store_and_decode(bsz, h_q, h_kv, d):
 
 
 @pytest.mark.parametrize("bsz", [16, 64, 1024])
-def test_fused_step(bsz):
-    case = W.decode_case(32, 8, 128, LENS, seed=95 + bsz, block_size=bsz)
+@pytest.mark.parametrize("h_q,h_kv,d", [(32, 8, 128), (16, 4, 64)])
+def test_fused_step(bsz, h_q, h_kv, d):
+    case = W.decode_case(h_q, h_kv, d, LENS, seed=95 + bsz, block_size=bsz)
     print("block size %d fused step" % bsz, flush=True)
     slots = _slots(case, case.context_lens)
     kc0, vc0 = poison_unused(case.k_cache, case.v_cache, case.block_tables, case.starts, bsz)
