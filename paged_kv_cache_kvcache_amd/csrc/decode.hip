@@ -192,10 +192,128 @@ __device__ __forceinline__ void issue_chunk_groups(const char* kc, const char* v
   for (int u = 0; u < U; ++u) vr[u] = load16(vc + off[u] + lane_off);
 }
 
+#ifndef PA_DECODE_TRANSPOSE
+#define PA_DECODE_TRANSPOSE 1
+#endif
+
+// DPP lane maps inside a 16-lane row (checked on gfx950): lane i reads lane
+// i^1, i^2, i^7 (mirror inside each 8-lane half) or i^8 (rotate by 8), or
+// lane n of its row (broadcast).
+constexpr int kDppXor1 = kDppQuadXor1;
+constexpr int kDppXor2 = kDppQuadXor2;
+constexpr int kDppXor7 = kDppRowHalfMirror;
+constexpr int kDppXor8 = kDppRowRor8;
+constexpr int kDppBcast0 = 0x150;  // row_newbcast:n is kDppBcast0 + n
+
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, Ctrl, 0xF, 0xF, true);
+}
+
+// keep + the partner's `send`, where a lane whose selector bit is set keeps
+// the upper value of the pair and sends the lower one (and the reverse).
+template <int Ctrl>
+__device__ __forceinline__ float fold(float lo, float hi, bool sel) {
+  const float keep = sel ? hi : lo;
+  const float send = sel ? lo : hi;
+  return keep + dpp<Ctrl>(send);
+}
+
+// compute_chunk for 16 lanes per kv-head vector (d = 128) and 4 or 8 loads
+// per chunk: the 16-lane sums of the U partial dot products are folded so
+// that each lane ends with the full score of ONE token (a transposed
+// butterfly: every exchange halves the values a lane keeps), so the softmax
+// runs one exponential per lane and head instead of U. With lane bits
+// b0, b1, b2 of the lane inside its 8-lane half, the lane holds token
+//   U = 8: u = 4*b2 + 2*b1 + b0      U = 4: u = 2*b2 + b0.
+// Tokens 2k and 2k+1 sit in lanes i and i^1: their weights are packed into
+// one bf16 pair there and broadcast to the row for the P.V products.
+template <class S, int D, int G, int U, bool TAIL>
+__device__ __forceinline__ void compute_chunk_t(SplitState<D, G>& st, float scale_log2, int row,
+                                                int nvalid, const uint4 (&kr)[U],
+                                                const uint4 (&vr)[U]) {
+  static_assert(S::LPT == 16 && (U == 4 || U == 8), "16-lane vectors, 4 or 8 loads");
+  const int lane = threadIdx.x;
+  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
+  const int u_me = U == 8 ? (b2 ? 4 : 0) + (b1 ? 2 : 0) + (b0 ? 1 : 0) : (b2 ? 2 : 0) + (b0 ? 1 : 0);
+  float sc[G];  // this lane's token's raw q.k per head
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = dot8_bf16(kr[u], st.qv[h], 0.f);
+    float y;
+    if constexpr (U == 8) {
+      float y1[4], y2[2];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y1[k] = fold<kDppXor7>(x[k], x[k + 4], b2);   // u bit 2
+#pragma unroll
+      for (int k = 0; k < 2; ++k) y2[k] = fold<kDppXor2>(y1[k], y1[k + 2], b1);  // u bit 1
+      y = fold<kDppXor1>(y2[0], y2[1], b0);                                        // u bit 0
+    } else {
+      float y1[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) y1[k] = fold<kDppXor7>(x[k], x[k + 2], b2);  // u bit 1
+      y = fold<kDppXor1>(y1[0], y1[1], b0);                                      // u bit 0
+      y += dpp<kDppXor2>(y);
+    }
+    y += dpp<kDppXor8>(y);
+    if constexpr (TAIL) y = (u_me * S::TPI + row < nvalid) ? y : -INFINITY;
+    sc[h] = y;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    // chunk max over the row's tokens (all 8 lanes of the half row)
+    float mx = fmaxf(sc[h], dpp<kDppXor1>(sc[h]));
+    if constexpr (U == 8) mx = fmaxf(mx, dpp<kDppXor2>(mx));
+    mx = fmaxf(mx, dpp<kDppXor7>(mx));
+    const float mnew = fmaxf(st.m[h], mx * scale_log2);  // scale > 0 commutes with max
+    const float msafe = (mnew == -INFINITY) ? 0.f : mnew;  // this row has seen no token yet
+    const float alpha = fast_exp2(st.m[h] - msafe);
+    st.l[h] *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[h][e] *= alpha;
+    st.m[h] = mnew;
+    const float p = fast_exp2(fmaf(sc[h], scale_log2, -msafe));
+    // (p of token 2k, p of token 2k+1) as one bf16 pair, then to every lane
+    const float pp = dpp<kDppXor1>(p);
+    const uint32_t pk = pack2_bf16_hw(b0 ? pp : p, b0 ? p : pp);
+    uint32_t ppair[U / 2];
+    if constexpr (U == 8) {
+      ppair[0] = dpp_u32<kDppBcast0 + 0>(pk);
+      ppair[1] = dpp_u32<kDppBcast0 + 2>(pk);
+      ppair[2] = dpp_u32<kDppBcast0 + 4>(pk);
+      ppair[3] = dpp_u32<kDppBcast0 + 6>(pk);
+    } else {
+      ppair[0] = dpp_u32<kDppBcast0 + 0>(pk);
+      ppair[1] = dpp_u32<kDppBcast0 + 4>(pk);
+    }
+    // P.V on token pairs with v_dot2_f32_bf16; the sum adds the same rounded
+    // weights, so the output stays an exact weighted mean
+#pragma unroll
+    for (int k = 0; k < U / 2; ++k) {
+      st.l[h] += bf16_lo(ppair[k]) + bf16_hi(ppair[k]);
+      const uint32_t a4[4] = {vr[2 * k].x, vr[2 * k].y, vr[2 * k].z, vr[2 * k].w};
+      const uint32_t c4[4] = {vr[2 * k + 1].x, vr[2 * k + 1].y, vr[2 * k + 1].z, vr[2 * k + 1].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = __builtin_amdgcn_perm(c4[w], a4[w], 0x05040100u);  // element 2w
+        const uint32_t hi = __builtin_amdgcn_perm(c4[w], a4[w], 0x07060302u);  // element 2w+1
+        st.acc[h][2 * w] = dot2_bf16(lo, ppair[k], st.acc[h][2 * w]);
+        st.acc[h][2 * w + 1] = dot2_bf16(hi, ppair[k], st.acc[h][2 * w + 1]);
+      }
+    }
+  }
+}
+
 template <class S, int D, int G, int U, bool TAIL>
 __device__ __forceinline__ void compute_chunk(SplitState<D, G>& st, float scale_log2, int row,
                                               int nvalid, const uint4 (&kr)[U],
                                               const uint4 (&vr)[U]) {
+  if constexpr (PA_DECODE_TRANSPOSE && S::LPT == 16 && (U == 4 || U == 8)) {
+    compute_chunk_t<S, D, G, U, TAIL>(st, scale_log2, row, nvalid, kr, vr);
+    return;
+  }
   float s[U][G];  // raw q.k (unscaled)
 #pragma unroll
   for (int u = 0; u < U; ++u) {
