@@ -8,27 +8,29 @@
 // "Nano-vLLM 源码解读 - 3. PagedAttention", §3).
 //
 // How (MI355X design, not the sketch's):
-//   * split-K: a work item is (sequence, kv-head, partition of 256-token
-//     units; up to 8 units, chosen from the batch), one wave64 each; a second kernel merges
-//     the partitions' (max, sum, unnormalised output) triples exactly.
-//     Sequences that fit one partition are finished by the first kernel.
-//     Items are dispatched highest partition first, so the grid drains on the
-//     first partitions that every sequence has instead of on a few long ones.
-//   * GQA: the wave loads each K/V row of its kv-head once and applies it to
-//     all G q-heads of the group held in registers (one load, G uses).
+//   * split-K: a work item is (sequence, group of KPW adjacent kv-heads,
+//     partition of up to 16 units of 256 tokens, sized from the batch), one
+//     wave64 each; a second kernel merges the partitions' (max, sum,
+//     unnormalised output) triples exactly. Sequences that fit one
+//     partition are finished by the first kernel.
+//   * dispatch: items longest first (each wave ranks the items from the
+//     sequence lengths), so the bandwidth-bound grid drains on short items;
+//     very large batches keep the plain order (highest partition first).
+//   * GQA: each lane holds the G q-heads of its kv-head, so one K/V load
+//     serves G heads.
 //   * loads: 16 bytes per lane, nontemporal (K/V are read once); d/8 lanes
-//     cover one token's 2*d-byte head vector, so a wave instruction reads
-//     64/(d/8) whole token vectors (4 at d = 128). Eight such loads of K and
-//     eight of V are in flight per wave before any arithmetic; full chunks
-//     address them from a wave-uniform base plus one per-lane offset (one
-//     table lookup per chunk; per group of TPI tokens when blocks are
-//     smaller than a chunk).
+//     cover one kv-head vector and KPW adjacent kv-heads make a 512-byte
+//     contiguous piece of a token row. Eight loads of K and eight of V are
+//     in flight per wave, and the next chunk's loads are issued before the
+//     current chunk is multiplied (two register buffers).
 //   * q.k: v_dot2_f32_bf16 on the raw bf16 pairs (exact products, fp32 sum),
-//     then a DPP butterfly over the d/8 lanes of the token (no LDS traffic).
+//     then DPP exchanges (no LDS); at d = 128 a transposed butterfly leaves
+//     each lane with one token's full score.
 //   * softmax: base-2 exponent (raw v_exp_f32) with scale*log2(e) folded into
-//     one FMA; each token-row of lanes keeps its own running max so no
-//     cross-row exchange is needed inside the loop; rows merge once at the end.
-//   * V: bf16 -> fp32 by shift/mask (exact), fp32 FMA accumulation.
+//     one FMA; each token-row of lanes keeps its own running max; rows merge
+//     once at the end.
+//   * P.V: weights rounded to bf16 pairs, v_dot2_f32_bf16 on paired V rows,
+//     fp32 accumulation; the sum adds the same rounded weights.
 #include <cmath>
 
 #include "common.hpp"
@@ -65,6 +67,7 @@ struct DecodeArgs {
   int32_t max_parts;
   int32_t block_size;   // tokens per physical block (power of two)
   int32_t block_shift;  // log2(block_size)
+  int32_t ordered;      // dispatch items longest first (find_item)
   float scale_log2;
 };
 
@@ -388,8 +391,13 @@ __device__ __forceinline__ void compute_chunk(SplitState<D, G>& st, float scale_
   }
 }
 
-#ifndef PA_DECODE_ORDER
-#define PA_DECODE_ORDER 1
+// Longest-first ordering costs every wave two passes over the sequence
+// lengths; beyond this many sequences (many short ones) that costs more than
+// the balance gains (measured: 4,096 sequences of <= 300 tokens took 447 us
+// unordered, 770 us ordered), and the grid, with many more items than
+// slots, balances itself.
+#ifndef PA_DECODE_ORDER_MAX_SEQS
+#define PA_DECODE_ORDER_MAX_SEQS 1024
 #endif
 
 // Dispatch order of the split kernel's work items, longest first. The
@@ -492,20 +500,18 @@ void decode_split_kernel(DecodeArgs a) {
   const int H_kv = a.num_kv_heads;
   const int H_q = H_kv * G;
   const int n_groups = H_kv / KPW;  // kv-head groups (the host checks divisibility)
-#if PA_DECODE_ORDER
-  // items longest first (find_item); the kv-head groups of one item are adjacent
-  const int gw = blockIdx.x % n_groups;
+  const int gw = blockIdx.x % n_groups;  // the kv-head groups of one item are adjacent
   int b, part;
-  if (!find_item(a, blockIdx.x / n_groups, b, part)) return;
+  if (a.ordered) {
+    // items longest first (find_item)
+    if (!find_item(a, blockIdx.x / n_groups, b, part)) return;
+  } else {
+    // highest partition first
+    const int idx = blockIdx.x / n_groups;
+    b = idx % a.num_seqs;
+    part = a.max_parts - 1 - idx / a.num_seqs;
+  }
   __builtin_amdgcn_sched_barrier(0);  // keep the item search apart from the main loop
-#else
-  // highest partition first
-  int idx = blockIdx.x;
-  const int gw = idx % n_groups;
-  idx /= n_groups;
-  const int b = idx % a.num_seqs;
-  const int part = a.max_parts - 1 - idx / a.num_seqs;
-#endif
   const int lane = threadIdx.x;
   const int sub = lane % LPT;                 // which 8 elements of the head vector
   const int g = gw * KPW + (lane / LPT) % KPW;  // this lane's kv-head
@@ -861,6 +867,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.max_parts = plan.max_parts;
   a.block_size = desc->block_size;
   a.block_shift = log2_int(desc->block_size);
+  a.ordered = num_seqs <= PA_DECODE_ORDER_MAX_SEQS;
   a.scale_log2 = scale * kLog2e;
 
   hipStream_t s = (hipStream_t)stream;

@@ -184,3 +184,19 @@ def test_prefill_store_bit_exact():
     torch.cuda.synchronize()
     kref, vref = oracle.store_kv(case.k_cache, case.v_cache, case.k_new, case.v_new, slots)
     assert np.array_equal(host_bits(kc), kref) and np.array_equal(host_bits(vc), vref)
+
+
+def test_large_batch_of_short_sequences_plain_order():
+    """Over 1,024 sequences the split kernel keeps the plain dispatch order
+    (highest partition first) instead of ranking items by length; lengths
+    1..600 with a few padding rows, sampled rows and every padding row vs
+    the oracle."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 600 + 1, size=1536)
+    lens[[3, 700, 1535]] = 0
+    case = W.decode_case(32, 8, 128, lens, seed=78)
+    out, caches, slots, before = run_decode_step(case)
+    kc_ref, vc_ref = check_store(case, caches, slots, before)
+    rows = sorted(set(rng.choice(len(lens), 40, replace=False).tolist()) | {3, 700, 1535})
+    check_decode(case, out, kc_ref, vc_ref, rows=rows)
+    assert np.all(out[[3, 700, 1535]] == 0)
