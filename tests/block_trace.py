@@ -114,3 +114,23 @@ def check_shared_blocks(make_bm, seed=0):
     assert a.block_table == g["tables"]["A"] and b.block_table == g["tables"]["B"]
     assert st["free"] == g["free"] and st["ref_count"] == g["ref_count"]
     assert st["index"] == index_of({"A": a, "B": b}, g["index"])
+
+
+def check_remainder_after_hit(bm_cls):
+    """A 500-token prompt whose first 256 tokens were hashed by an earlier
+    prompt: one cached block, so 500 - 256 = 244 tokens are left to prefill
+    ("12. 推理加速(二): nano-vllm — 1200 行手写 vLLM", §12.9 Scheduler,
+    the num_tokens example)."""
+    rng = np.random.default_rng(5)
+    first = tokens(rng, 256)
+    bm = bm_cls(8, 256)
+    a = Seq(first + tokens(rng, 44), 256)
+    bm.allocate(a, bm.can_allocate(a))
+    bm.hash_blocks(a, len(a))
+    a.num_cached_tokens = len(a)
+    b = Seq(first + tokens(rng, 244), 256)
+    hits = bm.can_allocate(b)
+    assert hits == 1
+    bm.allocate(b, hits)
+    assert b.num_cached_tokens == 256 and len(b) - b.num_cached_tokens == 244
+    assert b.block_table[0] == a.block_table[0] and len(b.block_table) == 2

@@ -36,6 +36,7 @@ def test_trace_of_seven_rounds():
 def test_prefix_hit_and_shared_blocks():
     T.check_prefix_hit(BlockManager)
     T.check_shared_blocks(BlockManager)
+    T.check_remainder_after_hit(BlockManager)
 
 
 def _same_state(a, b, where):

@@ -64,3 +64,8 @@ def test_new_block_exactly_after_a_full_one(n):
     before = len(s.block_table)
     bm.may_append(s)
     assert len(s.block_table) == before + (1 if (n + 1) % 256 == 1 else 0)
+
+
+
+def test_prefix_hit_leaves_the_rest_to_prefill():
+    T.check_remainder_after_hit(BlockManager)

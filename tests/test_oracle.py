@@ -302,6 +302,34 @@ def test_decode_equals_prefill_with_one_query():
     np.testing.assert_allclose(pre, dec, rtol=0, atol=1e-14)
 
 
+def test_split_combine_equals_single_pass():
+    """The decode kernels split a sequence into partitions and merge the
+    per-partition (max, sum, unnormalised output) triples; in base 2:
+    M = max m_p, L = sum l_p 2^(m_p - M), out = sum o_p 2^(m_p - M) / L.
+    Written out here in fp64 over uneven splits, it must equal the oracle's
+    single pass over the whole sequence."""
+    case = W.decode_case(8, 2, 64, [1000], seed=46)
+    ref = oracle.decode_one(case.q[0], case.k_cache, case.v_cache, case.block_tables[0], 1000,
+                            case.scale)
+    keys = oracle.gather_rows(case.k_cache, case.block_tables[0], 1000)
+    vals = oracle.gather_rows(case.v_cache, case.block_tables[0], 1000)
+    q = f64(case.q[0])
+    c = case.scale / math.log(2.0)  # scores in log2 units
+    for cuts in ([0, 1000], [0, 256, 1000], [0, 1, 2, 999, 1000], [0, 300, 301, 700, 1000]):
+        for h in range(8):
+            g = h // 4
+            parts = []
+            for lo, hi in zip(cuts[:-1], cuts[1:]):
+                s2 = (keys[lo:hi, g, :] @ q[h]) * c
+                m = s2.max()
+                w = np.exp2(s2 - m)
+                parts.append((m, w.sum(), w @ vals[lo:hi, g, :]))
+            M = max(m for m, _, _ in parts)
+            L = sum(l * 2.0 ** (m - M) for m, l, _ in parts)
+            out = sum(o * 2.0 ** (m - M) for m, _, o in parts) / L
+            np.testing.assert_allclose(out, ref[h], rtol=0, atol=1e-12)
+
+
 def test_shared_prefix_rows_identical_across_sequences():
     """Sequences whose tables share the prefix blocks: prefix queries see only
     prefix keys (causality), so their outputs agree across sequences."""
