@@ -239,6 +239,10 @@ def main() -> int:
                          "pa_store_kv then pa_decode")
     ap.add_argument("--graph", action="store_true",
                     help="capture the step in a HIP graph and time its replays")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="copies of the KV pool read in turn by consecutive steps (0: 2 when "
+                         "the batch's K/V are under 2 GiB, so the last-level cache cannot serve "
+                         "a step from the previous one; 1 with --graph)")
     ap.add_argument("--block-size", type=int, default=256,
                     help="tokens per cache block (power of two, 16..1024); same lengths")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -289,15 +293,23 @@ def main() -> int:
     ws_bytes = B.pa_decode_workspace_size(case.num_q_heads, kc, case.batch, max_ctx)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
-    def store():
-        B.pa_store_kv(k_new, v_new, kc, vc, slots_d)
+    # A batch whose K/V fit a few times into the 256 MB last-level cache (MALL)
+    # would be partly served from it on back-to-back steps; consecutive steps
+    # then read different copies of the pool.
+    kv_bytes = decode_bytes(case)
+    replicas = 1 if args.graph else (args.replicas or (1 if kv_bytes >= (2 << 30) else 2))
+    pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(replicas - 1)]
+    turn = [0]
 
-    def decode():
-        B.pa_decode(q, kc, vc, bt_d, ctx_d, case.scale, out, max_context_len=max_ctx,
+    def store(pool):
+        B.pa_store_kv(k_new, v_new, pool[0], pool[1], slots_d)
+
+    def decode(pool):
+        B.pa_decode(q, pool[0], pool[1], bt_d, ctx_d, case.scale, out, max_context_len=max_ctx,
                     workspace=ws)
 
-    def fused():
-        B.pa_decode_step(q, k_new, v_new, kc, vc, slots_d, bt_d, ctx_d, case.scale, out,
+    def fused(pool):
+        B.pa_decode_step(q, k_new, v_new, pool[0], pool[1], slots_d, bt_d, ctx_d, case.scale, out,
                          max_context_len=max_ctx, workspace=ws)
 
     if args.mode == "fused":
@@ -305,9 +317,15 @@ def main() -> int:
     else:
         calls = [("pa_store_kv", store), ("pa_decode", decode)]
 
+    def next_pool():
+        pool = pools[turn[0] % len(pools)]
+        turn[0] += 1
+        return pool
+
     def step():
+        pool = next_pool()
         for _, fn in calls:
-            fn()
+            fn(pool)
 
     for _ in range(args.warmup):
         step()
@@ -345,9 +363,10 @@ def main() -> int:
           for _ in range(n)]
     torch.cuda.synchronize(dev)
     for i in range(n):
+        pool = next_pool()
         ev[i][0].record()
         for j, (_, fn) in enumerate(calls):
-            fn()
+            fn(pool)
             ev[i][j + 1].record()
     torch.cuda.synchronize(dev)
     ms_call = {name: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / n
@@ -382,7 +401,7 @@ def main() -> int:
                        "B 256", "B %d" % case.block_size) + "; step = store of the batch's "
                    "new tokens + decode, one layer", "global_batch": case.batch,
                    "seq_len": max_ctx, "parallelism": "none (1 GPU)",
-                   "block_size": case.block_size,
+                   "block_size": case.block_size, "pool_replicas": len(pools),
                    "step_mode": args.mode + (" + hip graph" if args.graph else "")},
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": {"per_layer": round(case.batch / (ms_step * 1e-3), 1),
