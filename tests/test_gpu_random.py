@@ -1,0 +1,124 @@
+"""Randomised GPU parity sweep: seeded draws of head counts, head size,
+group size, block size, batch, lengths (empty rows included), prefix
+lengths and split-K partition sizes, through every attention entry point
+(pa_decode, pa_decode_partitioned, pa_decode_step, pa_prefill_varlen,
+pa_mixed_varlen), each against the fp64 oracle over every row (store
+bit-exact; attention max-abs 1e-2 / mean-abs 1e-3)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import assert_close, dev_bf16, dev_i32, host_bits, host_f64, poison_unused
+from paged_kv_cache_kvcache_amd import binding as B
+from paged_kv_cache_kvcache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.load()
+
+
+def _shape(rng):
+    d = int(rng.choice([64, 128]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    h_kv = int(rng.choice([1, 2, 3, 4, 8]))
+    bsz = int(rng.choice([16, 32, 64, 128, 256, 512, 1024]))
+    return g * h_kv, h_kv, d, bsz
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_decode(seed):
+    rng = np.random.default_rng(5000 + seed)
+    h_q, h_kv, d, bsz = _shape(rng)
+    n = int(rng.integers(1, 13))
+    lens = rng.integers(1, 3000, size=n)
+    lens[rng.random(n) < 0.15] = 0  # graph-padding rows
+    entry = ["pa_decode", "pa_decode_partitioned", "pa_decode_step"][seed % 3]
+    pb = int(rng.choice([1, 2, 5])) if entry == "pa_decode_partitioned" else 0
+    case = W.decode_case(h_q, h_kv, d, lens, seed=6000 + seed, block_size=bsz)
+    print("seed %d: %s H=%d/%d d=%d B=%d lens=%s part=%d" % (
+        seed, entry, h_q, h_kv, d, bsz, lens.tolist(), pb), flush=True)
+    full = np.full(n, -1, dtype=np.int32)
+    if (lens > 0).any():
+        slots, _, _ = B.pa_build_metadata(case.block_tables, case.starts, case.context_lens, bsz)
+        full[lens > 0] = slots
+    kc0, vc0 = poison_unused(case.k_cache, case.v_cache, case.block_tables, case.starts, bsz)
+    kc, vc = dev_bf16(kc0), dev_bf16(vc0)
+    q = dev_bf16(case.q)
+    out = torch.empty_like(q)
+    max_ctx = int(lens.max())
+    if entry == "pa_decode_step":
+        B.pa_decode_step(q, dev_bf16(case.k_new), dev_bf16(case.v_new), kc, vc, dev_i32(full),
+                         dev_i32(case.block_tables), dev_i32(case.context_lens), case.scale, out,
+                         max_context_len=max_ctx)
+    else:
+        B.pa_store_kv(dev_bf16(case.k_new), dev_bf16(case.v_new), kc, vc, dev_i32(full))
+        B.pa_decode(q, kc, vc, dev_i32(case.block_tables), dev_i32(case.context_lens),
+                    case.scale, out, max_context_len=max_ctx, partition_blocks=pb)
+    torch.cuda.synchronize()
+    kref, vref = oracle.store_kv(kc0, vc0, case.k_new, case.v_new, full)
+    assert np.array_equal(host_bits(kc), kref) and np.array_equal(host_bits(vc), vref)
+    ref = oracle.decode(case.q, kref, vref, case.block_tables, case.context_lens, case.scale)
+    got = host_f64(out)
+    assert np.all(got[lens == 0] == 0)
+    mx, mean = assert_close(got, ref, "random decode %d" % seed)
+    print("  max abs %.3g mean abs %.3g" % (mx, mean), flush=True)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_prefill(seed):
+    rng = np.random.default_rng(7000 + seed)
+    h_q, h_kv, d, bsz = _shape(rng)
+    n = int(rng.integers(1, 7))
+    mixed = seed % 2 == 1
+    n_dec = int(rng.integers(0, 5)) if mixed else 0
+    prefix = rng.integers(0, 1500, size=n + n_dec)
+    suffix = rng.integers(1, 300, size=n + n_dec)
+    suffix[:n_dec] = 1  # decode rows lead a mixed batch
+    prefix[:n_dec] += 1
+    starts = prefix.astype(np.int32)
+    ends = (prefix + suffix).astype(np.int32)
+    need = [W.blocks_needed(int(e), bsz) for e in ends]
+    nb = int(np.ceil(1.1 * sum(need))) + 1
+    perm = rng.permutation(nb)
+    tables, pos = [], 0
+    for k in need:
+        tables.append(perm[pos:pos + k].tolist())
+        pos += k
+    total = int(suffix.sum())
+    case = W.PrefillCase("random", h_q, h_kv, d, bsz, nb,
+                         W.normal_bf16(rng, (total, h_q, d)),
+                         W.normal_bf16(rng, (total, h_kv, d)),
+                         W.normal_bf16(rng, (total, h_kv, d)),
+                         W.normal_bf16(rng, (nb, bsz, h_kv, d)),
+                         W.normal_bf16(rng, (nb, bsz, h_kv, d)),
+                         W.pad_tables(tables), starts, ends, 1.0 / np.sqrt(d), seed)
+    entry = "pa_mixed_varlen" if mixed else "pa_prefill_varlen"
+    print("seed %d: %s H=%d/%d d=%d B=%d decode rows %d prefix=%s suffix=%s" % (
+        seed, entry, h_q, h_kv, d, bsz, n_dec, prefix.tolist(), suffix.tolist()), flush=True)
+    slots, cu_q, cu_k = B.pa_build_metadata(case.block_tables, starts, ends, bsz)
+    kc0, vc0 = poison_unused(case.k_cache, case.v_cache, case.block_tables, starts, bsz)
+    kc, vc = dev_bf16(kc0), dev_bf16(vc0)
+    B.pa_store_kv(dev_bf16(case.k_new), dev_bf16(case.v_new), kc, vc, dev_i32(slots))
+    q = dev_bf16(case.q)
+    out = torch.empty_like(q)
+    args = (q, kc, vc, dev_i32(cu_q), dev_i32(cu_k))
+    if mixed:
+        B.pa_mixed_varlen(*args, n_dec, int(suffix.max()), int(ends.max()),
+                          dev_i32(case.block_tables), case.scale, out)
+    else:
+        B.pa_prefill_varlen(*args, int(suffix.max()), int(ends.max()),
+                            dev_i32(case.block_tables), case.scale, out)
+    torch.cuda.synchronize()
+    kref, vref = oracle.store_kv(kc0, vc0, case.k_new, case.v_new, slots)
+    assert np.array_equal(host_bits(kc), kref) and np.array_equal(host_bits(vc), vref)
+    ref = oracle.prefill_varlen(case.q, kref, vref, cu_q, cu_k, case.block_tables, case.scale)
+    mx, mean = assert_close(host_f64(out), ref, "random prefill %d" % seed)
+    print("  max abs %.3g mean abs %.3g" % (mx, mean), flush=True)
