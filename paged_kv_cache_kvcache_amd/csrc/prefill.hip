@@ -7,10 +7,10 @@
 // sits at position k_len - q_len + i and attends to keys 0 .. that position.
 //
 // How (MI355X design):
-//   * Work item = workgroup of 4 waves for (sequence, kv-head, block of
-//     256/G query positions). Its 16 MFMA column tiles are 16 positions x 1
-//     q-head each, covering all G q-heads of the kv-head, so every K/V tile
-//     staged in LDS serves the whole GQA group.
+//   * Work item = workgroup of 8 waves for (sequence, kv-head, block of
+//     256/G query positions). Its 16 MFMA column tiles (two per wave) are 16
+//     positions x 1 q-head each, covering all G q-heads of the kv-head, so
+//     every K/V tile staged in LDS serves the whole GQA group.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_16x16x32_bf16: A = K rows from LDS, B = Q held in registers
 //     for the whole loop. The accumulator layout of S^T (one query column per
@@ -22,9 +22,9 @@
 //     folded in, running max exchanged across the 4 lane groups of a column,
 //     P rounded to bf16 for the MFMA (the row sum adds the same rounded
 //     weights), fp32 accumulation, bf16 output.
-//   * Keys are staged 64 at a time (a stage never straddles a 256-token block,
-//     so one block-table lookup per stage), double-buffered in LDS with
-//     register staging two stages ahead of the multiply.
+//   * Keys are staged 64 at a time (with blocks of 64 tokens or more a stage
+//     never straddles a block, so one block-table lookup per stage),
+//     double-buffered in LDS with register staging one stage ahead of LDS.
 //   * Causal work skipping: stages past the work item's last query are never
 //     loaded; a wave skips the stages that lie after all its queries; only
 //     stages that cross the diagonal apply the mask.
@@ -275,122 +275,119 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     for (int mt = 0; mt < MT; ++mt) o[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Register staging two stages deep: while stage st is multiplied, stage
-  // st+1 (issued an iteration earlier) lands and stage st+2 is issued. Stage
-  // indices are clamped, so every issue is unconditional and the memory
-  // counter waits stay static.
-  u32x4 kra[GG::KCHUNKS], krb[GG::KCHUNKS];
-  typename VVec<GG::VW>::T vra[2], vrb[2];
-  load_stage<D, SMALL>(a, bt, g, kmax, 0, kra, vra);
-  store_stage<D>(lds, kra, vra);
-  load_stage<D, SMALL>(a, bt, g, kmax, min(1, n_stages - 1), kra, vra);
-  __syncthreads();
-
-  // One stage: issue the loads of stage st+2 into `next`, multiply the LDS
-  // copy of stage st, then copy `ready` (stage st+1) into the other buffer.
-  auto stage_step = [&](int st, const u32x4 (&kready)[GG::KCHUNKS],
-                        const typename VVec<GG::VW>::T (&vready)[2], u32x4 (&knext)[GG::KCHUNKS],
-                        typename VVec<GG::VW>::T (&vnext)[2]) {
-    load_stage<D, SMALL>(a, bt, g, kmax, min(st + 2, n_stages - 1), knext, vnext);
-    const char* ks_lds = lds + (st & 1) * GG::STAGE;
-    const char* vt_lds = ks_lds + GG::KBYTES;
-    const int key0 = st * kKT;  // absolute position of the stage's first key
-    if (key0 <= off + wmax) {   // else every key is after every query of the wave
-      // ---- S^T = K Q^T for the stage's 64 keys x (kNT x 16) columns
-      f32x4 s[kKT / 16][kNT];
+  // S^T = K Q^T for the 64 keys of the stage held in `kst` x (kNT x 16) columns
+  auto scores = [&](const char* kst, f32x4 (&sc)[kKT / 16][kNT]) {
 #pragma unroll
-      for (int kt = 0; kt < kKT / 16; ++kt) {
+    for (int kt = 0; kt < kKT / 16; ++kt) {
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) s[kt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const char* arow = ks_lds + (kt * 16 + col) * GG::KROW + grp * 16;
+      for (int j = 0; j < kNT; ++j) sc[kt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const char* arow = kst + (kt * 16 + col) * GG::KROW + grp * 16;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bf16x8 av =
-              __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + ks * 64));
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const bf16x8 av =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + ks * 64));
 #pragma unroll
-          for (int j = 0; j < kNT; ++j)
-            s[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[j][ks], s[kt][j], 0, 0, 0);
-        }
-      }
-      // ---- online softmax per column over the 64 keys; P^T operands for the
-      // two 32-key products (lane order of key_slot within each half)
-      bf16x8 pf[kNT][kKT / 32];
-#pragma unroll
-      for (int j = 0; j < kNT; ++j) {
-        const int qpos = off + pbase[j] + col;  // absolute position of this column's query
-        float sv[kKT / 4];
-#pragma unroll
-        for (int kt = 0; kt < kKT / 16; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sv[kt * 4 + i] = s[kt][j][i];
-        if (key0 + kKT - 1 > off + pbase[j]) {  // the stage crosses some column's diagonal
-#pragma unroll
-          for (int i = 0; i < kKT / 4; ++i) {
-            const int kpos = key0 + (i >> 2) * 16 + grp * 4 + (i & 3);
-            if (kpos > qpos) sv[i] = -INFINITY;
-          }
-        }
-        float mx = sv[0];
-#pragma unroll
-        for (int i = 1; i < kKT / 4; ++i) mx = fmaxf(mx, sv[i]);
-        mx = fmaxf(mx, xor_lane(mx, 16));
-        mx = fmaxf(mx, xor_lane(mx, 32));
-        mx *= a.scale_log2;
-#if PA_PREFILL_LAZY
-        // all lanes of a column see the same mx and m, so they agree on it
-        if (mx > m[j] + kLazyLog2) {
-#else
-        {
-#endif
-          const float mnew = fmaxf(m[j], mx);
-          const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);  // 0 on the first step
-          m[j] = mnew;
-          l[j] *= alpha;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) o[j][mt] *= alpha;
-        }
-        const float negm = (m[j] == -INFINITY) ? 0.f : -m[j];
-#pragma unroll
-        for (int h = 0; h < kKT / 32; ++h) {
-          float p[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            p[i] = __builtin_amdgcn_exp2f(fmaf(sv[h * 8 + i], a.scale_log2, negm));
-          uint4 pk;
-          pk.x = pack2_bf16(p[0], p[1]);
-          pk.y = pack2_bf16(p[2], p[3]);
-          pk.z = pack2_bf16(p[4], p[5]);
-          pk.w = pack2_bf16(p[6], p[7]);
-          // the sum adds the rounded weights the MFMA sees (an exact weighted
-          // mean): a dot product of each packed pair with (1, 1)
-          l[j] = sum_pair_bf16(pk.x, l[j]);
-          l[j] = sum_pair_bf16(pk.y, l[j]);
-          l[j] = sum_pair_bf16(pk.z, l[j]);
-          l[j] = sum_pair_bf16(pk.w, l[j]);
-          pf[j][h] = __builtin_bit_cast(bf16x8, pk);
-        }
-      }
-      // ---- O^T += V^T P^T, two 32-key products
-#pragma unroll
-      for (int h = 0; h < kKT / 32; ++h) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const char* vrow = vt_lds + (mt * 16 + col) * GG::VROW + (h * 32 + grp * 8) * 2;
-          const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vrow));
-#pragma unroll
-          for (int j = 0; j < kNT; ++j)
-            o[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf[j][h], o[j][mt], 0, 0, 0);
-        }
+        for (int j = 0; j < kNT; ++j)
+          sc[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[j][ks], sc[kt][j], 0, 0, 0);
       }
     }
-
-    if (st + 1 < n_stages) store_stage<D>(lds + ((st + 1) & 1) * GG::STAGE, kready, vready);
-    __syncthreads();
   };
-  for (int st = 0; st < n_stages; st += 2) {
-    stage_step(st, kra, vra, krb, vrb);
-    if (st + 1 >= n_stages) break;
-    stage_step(st + 1, krb, vrb, kra, vra);
+  // Online softmax of the stage's scores per column, then O^T += V^T P^T
+  // with the stage's V^T held in `vst` (two 32-key products).
+  auto softmax_pv = [&](int key0, const f32x4 (&sc)[kKT / 16][kNT], const char* vst) {
+    // P^T operands for the two 32-key products (lane order of key_slot)
+    bf16x8 pf[kNT][kKT / 32];
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) {
+      const int qpos = off + pbase[j] + col;  // absolute position of this column's query
+      float sv[kKT / 4];
+#pragma unroll
+      for (int kt = 0; kt < kKT / 16; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[kt * 4 + i] = sc[kt][j][i];
+      if (key0 + kKT - 1 > off + pbase[j]) {  // the stage crosses some column's diagonal
+#pragma unroll
+        for (int i = 0; i < kKT / 4; ++i) {
+          const int kpos = key0 + (i >> 2) * 16 + grp * 4 + (i & 3);
+          if (kpos > qpos) sv[i] = -INFINITY;
+        }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int i = 1; i < kKT / 4; ++i) mx = fmaxf(mx, sv[i]);
+      mx = fmaxf(mx, xor_lane(mx, 16));
+      mx = fmaxf(mx, xor_lane(mx, 32));
+      mx *= a.scale_log2;
+#if PA_PREFILL_LAZY
+      // all lanes of a column see the same mx and m, so they agree on it
+      if (mx > m[j] + kLazyLog2) {
+#else
+      {
+#endif
+        const float mnew = fmaxf(m[j], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);  // 0 on the first step
+        m[j] = mnew;
+        l[j] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[j][mt] *= alpha;
+      }
+      const float negm = (m[j] == -INFINITY) ? 0.f : -m[j];
+#pragma unroll
+      for (int h = 0; h < kKT / 32; ++h) {
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          p[i] = __builtin_amdgcn_exp2f(fmaf(sv[h * 8 + i], a.scale_log2, negm));
+        uint4 pk;
+        pk.x = pack2_bf16(p[0], p[1]);
+        pk.y = pack2_bf16(p[2], p[3]);
+        pk.z = pack2_bf16(p[4], p[5]);
+        pk.w = pack2_bf16(p[6], p[7]);
+        // the sum adds the rounded weights the MFMA sees (an exact weighted
+        // mean): a dot product of each packed pair with (1, 1)
+        l[j] = sum_pair_bf16(pk.x, l[j]);
+        l[j] = sum_pair_bf16(pk.y, l[j]);
+        l[j] = sum_pair_bf16(pk.z, l[j]);
+        l[j] = sum_pair_bf16(pk.w, l[j]);
+        pf[j][h] = __builtin_bit_cast(bf16x8, pk);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kKT / 32; ++h) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const char* vrow = vst + (mt * 16 + col) * GG::VROW + (h * 32 + grp * 8) * 2;
+        const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vrow));
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+          o[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf[j][h], o[j][mt], 0, 0, 0);
+      }
+    }
+  };
+
+  // Register staging one stage ahead of LDS: at iteration st, stage st+1
+  // (loaded during the previous iteration) is copied into the LDS buffer of
+  // stage st-1, which every wave finished with before the last barrier, and
+  // stage st+2 is issued into the same registers, so its loads land while
+  // stage st is multiplied. Stage indices are clamped, so every issue is
+  // unconditional and the memory counter waits stay static.
+  u32x4 kr[GG::KCHUNKS];
+  typename VVec<GG::VW>::T vr[2];
+  load_stage<D, SMALL>(a, bt, g, kmax, 0, kr, vr);
+  store_stage<D>(lds, kr, vr);
+  load_stage<D, SMALL>(a, bt, g, kmax, min(1, n_stages - 1), kr, vr);
+  __syncthreads();
+  for (int st = 0; st < n_stages; ++st) {
+    if (st + 1 < n_stages) store_stage<D>(lds + ((st + 1) & 1) * GG::STAGE, kr, vr);
+    load_stage<D, SMALL>(a, bt, g, kmax, min(st + 2, n_stages - 1), kr, vr);
+    const char* ks_lds = lds + (st & 1) * GG::STAGE;
+    const int key0 = st * kKT;  // absolute position of the stage's first key
+    if (key0 <= off + wmax) {   // else every key is after every query of the wave
+      f32x4 s[kKT / 16][kNT];
+      scores(ks_lds, s);
+      softmax_pv(key0, s, ks_lds + GG::KBYTES);
+    }
+    __syncthreads();
   }
 
   // ---- epilogue: column sums across the 4 lane groups, normalise, store
