@@ -251,8 +251,8 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures the single-GPU path only; --gpus %d (WORLD_SIZE %d) is not "
-              "supported: this build has no multi-GPU path" % (args.gpus, world), file=sys.stderr)
+        print("bench.py measures one GPU; --gpus %d (WORLD_SIZE %d) is not supported: the "
+              "library has no multi-GPU path" % (args.gpus, world), file=sys.stderr)
         return 2
 
     import numpy as np
