@@ -377,10 +377,10 @@ def main() -> int:
     gbs = (db + sb) / (ms_step * 1e-3) / 1e9
     if args.mode == "fused":
         dom, dom_bytes = "pa_decode_step", db + sb
-        dom_desc = "pa_decode_step (store + split-K decode + merge)"
+        dom_desc = "pa_decode_step (order + store fused into split-K decode + merge)"
     else:
         dom, dom_bytes = "pa_decode", db
-        dom_desc = "pa_decode (split-K + merge)"
+        dom_desc = "pa_decode (order + split-K + merge)"
     dom_gbs = dom_bytes / (ms_call[dom] * 1e-3) / 1e9
     traffic = traffic_from_profile(PMC_FILE, DECODE_SRC, args.mode, args.block_size)
 

@@ -86,8 +86,11 @@ int pa_store_kv(const void* k, int64_t k_row_stride, const void* v, int64_t v_ro
 
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for
- * this batch geometry (split-K partial results). Returns 0 on invalid
- * arguments. The result depends only on the arguments.
+ * this batch geometry: split-K partial results when a sequence can span
+ * more than one partition, and a longest-first dispatch order when the
+ * grid has more work items than the GPU has compute units (at most 4096
+ * sequences). 0 when neither applies, and on invalid arguments. The result
+ * depends only on the arguments.
  */
 size_t pa_decode_workspace_size(const pa_desc* desc, int32_t num_seqs, int32_t max_context_len);
 

@@ -13,9 +13,14 @@
 //     wave64 each; a second kernel merges the partitions' (max, sum,
 //     unnormalised output) triples exactly. Sequences that fit one
 //     partition are finished by the first kernel.
-//   * dispatch: items longest first (each wave ranks the items from the
-//     sequence lengths), so the bandwidth-bound grid drains on short items;
-//     very large batches keep the plain order (highest partition first).
+//   * dispatch: when the grid has more items than CUs, a one-workgroup
+//     kernel first ranks them longest first, so long items are spread over
+//     the CUs and the bandwidth-bound grid drains on short ones; batches of
+//     more than 4,096 sequences keep the plain order (highest partition
+//     first).
+//   * loads in flight: at full occupancy a wave waits for a chunk's loads
+//     before issuing the next chunk's; with fewer waves two chunks overlap
+//     (the host picks the kernel).
 //   * GQA: each lane holds the G q-heads of its kv-head, so one K/V load
 //     serves G heads.
 //   * loads: 16 bytes per lane, nontemporal (K/V are read once); d/8 lanes
@@ -67,7 +72,7 @@ struct DecodeArgs {
   int32_t max_parts;
   int32_t block_size;   // tokens per physical block (power of two)
   int32_t block_shift;  // log2(block_size)
-  int32_t ordered;      // dispatch items longest first (find_item)
+  int32_t* order;  // dispatch order (decode_order_kernel), or null: plain order
   float scale_log2;
 };
 
@@ -92,15 +97,19 @@ __device__ __forceinline__ int clamp_len(int n, int max_blocks, int block_size) 
   return (int)max((int64_t)0, min((int64_t)n, (int64_t)max_blocks * block_size));
 }
 
-// Byte offset in a cache of token `pos` of a sequence: physical block through
-// the table, then the offset inside it. A broken entry (precondition
-// violated) reads block 0: the result is then meaningless, but the access
-// stays inside the pool.
-__device__ __forceinline__ int64_t token_offset(const DecodeArgs& a, const int32_t* bt, int pos,
+// Byte offset in a cache of token `pos` of a sequence, given the table entry
+// blk of its block: the physical block, then the offset inside it. A broken
+// entry (precondition violated) reads block 0: the result is then
+// meaningless, but the access stays inside the pool.
+__device__ __forceinline__ int64_t block_offset(const DecodeArgs& a, int blk, int pos,
                                                 int64_t row_bytes) {
-  int blk = bt[pos >> a.block_shift];
   blk = (blk >= 0 && blk < a.num_blocks) ? blk : 0;
   return (((int64_t)blk << a.block_shift) + (pos & (a.block_size - 1))) * row_bytes;
+}
+
+__device__ __forceinline__ int64_t token_offset(const DecodeArgs& a, const int32_t* bt, int pos,
+                                                int64_t row_bytes) {
+  return block_offset(a, bt[pos >> a.block_shift], pos, row_bytes);
 }
 
 #ifndef PA_DECODE_UNROLL
@@ -136,6 +145,29 @@ __device__ __forceinline__ uint4 load16(const char* p) {
 #ifndef PA_DECODE_PIPE
 #define PA_DECODE_PIPE 1
 #endif
+#ifndef PA_DECODE_DRAIN
+#define PA_DECODE_DRAIN 1
+#endif
+
+// Before a chunk's loads are issued (U loads each of K and V), optionally
+// wait until the previous chunk's loads have all arrived (s_waitcnt
+// vmcnt(0); the export and LDS/scalar counters are left alone), so a wave
+// has one chunk of loads in flight while it multiplies the chunk before.
+// Without the wait the compiler's partial waits inside the multiply let two
+// chunks' loads overlap. With every wave slot of the chip filled, the
+// overlap only adds requests to already full memory queues (measured 3%
+// slower); with fewer waves it is what keeps enough bytes in flight
+// (without it, up to twice as slow at one wave per SIMD), so the host
+// picks the kernel. Chunks of 4 loads never wait here.
+template <int U, bool DRAIN>
+__device__ __forceinline__ void drain_loads() {
+#if PA_DECODE_DRAIN
+  if constexpr (DRAIN && U == 8) {
+    __builtin_amdgcn_sched_barrier(0);  // not hoisted into the multiply before it
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
+#endif
+}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -391,101 +423,118 @@ __device__ __forceinline__ void compute_chunk(SplitState<D, G>& st, float scale_
   }
 }
 
-// Longest-first ordering costs every wave two passes over the sequence
-// lengths; beyond this many sequences (many short ones) that costs more than
-// the balance gains (measured: 4,096 sequences of <= 300 tokens took 447 us
-// unordered, 770 us ordered), and the grid, with many more items than
-// slots, balances itself.
-#ifndef PA_DECODE_ORDER_MAX_SEQS
-#define PA_DECODE_ORDER_MAX_SEQS 1024
-#endif
-
 // Dispatch order of the split kernel's work items, longest first. The
 // kernel is bandwidth-bound and its items differ in length (a sequence's
 // last partition is partial), so handing out the longest items first lets
 // the grid drain on short ones instead of ending on a few long stragglers.
-// Items are ranked by length bucket (32 buckets of part_tokens/32 tokens,
+// Items are ranked by length bucket (32 buckets of part_tokens/32 tokens;
 // full partitions in the top one; empty sequences, which only write zeros,
-// last), then by (sequence, partition). Every wave derives its own item
-// from the sequence lengths (a pass over them for the bucket histogram, a
-// second one to locate its rank inside the bucket), so no ordering kernel
-// or buffer is needed.
+// last), then by (sequence, partition). One workgroup ranks them before the
+// split kernel runs and writes order[rank] = (part << 12) | sequence, -1
+// past the last item; a split wave reads its one entry. (Each wave ranking
+// the items itself from the lengths cost it 8-24 us: every wave read the
+// same lengths.)
+#ifndef PA_DECODE_ORDER_MAX_SEQS
+#define PA_DECODE_ORDER_MAX_SEQS 4096  // sequence ids must fit 12 bits
+#endif
 constexpr int kOrderBuckets = 32;
+constexpr int kOrderThreads = 1024;
 
 __device__ __forceinline__ int len_bucket(int len, int part_tokens) {
   return 1 + (int)(((int64_t)(len - 1) * kOrderBuckets) / part_tokens);  // 1..32
 }
 
-// Items of sequence length n in bucket k (n already clamped to max_parts
-// partitions): full partitions sit in the top bucket, the partial last one
-// in its length's bucket, an empty sequence in bucket 0.
-__device__ __forceinline__ int items_in_bucket(int n, int k, int part_tokens) {
-  if (n == 0) return k == 0;
-  const int f = n / part_tokens, rem = n % part_tokens;
-  return (k == kOrderBuckets ? f : 0) + (rem > 0 && len_bucket(rem, part_tokens) == k);
-}
-
-// Finds the (sequence, partition) of rank r; false when r is past the last item.
-__device__ bool find_item(const DecodeArgs& a, int r, int& seq, int& part) {
-  __shared__ int hist[kOrderBuckets + 1];
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs a, int max_items) {
+  constexpr int NB = kOrderBuckets + 1;
+  constexpr int NW = kOrderThreads / kWave;
+  __shared__ int next[NB];           // first free rank of each bucket
+  __shared__ int wave_at[NW][NB];    // per round: a wave's item count, then first rank, per bucket
+  __shared__ int total;
+  const int t = threadIdx.x;
+  const int lane = t % kWave;
+  const int w = t / kWave;
   const int P = a.part_tokens;
-  const int cap = a.max_parts * P;  // a length beyond max_context_len is cut here
-  if (lane <= kOrderBuckets) hist[lane] = 0;
+  // a sequence's items: `top` in the top bucket (its full partitions, then
+  // a nearly full last one), and one more in bucket k < 32 (k = -1: none);
+  // `full` is its number of full partitions
+  auto items = [&](int s, int& full, int& top, int& k) {
+    const int n = clamp_len(seq_len(a, s), a.max_blocks, a.block_size);
+    const int np = min((n + P - 1) / P, a.max_parts);
+    full = min(n / P, np);
+    k = n == 0 ? 0 : (np > full ? len_bucket(n - full * P, P) : -1);
+    top = full + (k == kOrderBuckets);
+    if (k == kOrderBuckets) k = -1;
+  };
+  if (t < NB) next[t] = 0;
   __syncthreads();
-  for (int s = lane; s < a.num_seqs; s += kWave) {
-    const int n = min(clamp_len(seq_len(a, s), a.max_blocks, a.block_size), cap);
-    if (n == 0) {
-      atomicAdd(&hist[0], 1);
-    } else {
-      if (n / P) atomicAdd(&hist[kOrderBuckets], n / P);
-      if (n % P) atomicAdd(&hist[len_bucket(n % P, P)], 1);
+  for (int s = t; s < a.num_seqs; s += kOrderThreads) {
+    int full, top, k;
+    items(s, full, top, k);
+    if (top) atomicAdd(&next[kOrderBuckets], top);
+    if (k >= 0) atomicAdd(&next[k], 1);
+  }
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int k = kOrderBuckets; k >= 0; --k) {
+      const int c = next[k];
+      next[k] = run;
+      run += c;
     }
+    total = run;
   }
-  __syncthreads();
-  int k = kOrderBuckets;
-  for (; k >= 0; --k) {
-    const int c = hist[k];
-    if (r < c) break;
-    r -= c;
-  }
-  if (k < 0) return false;
-  // the r-th item of bucket k in (sequence, partition) order
-  for (int base = 0; base < a.num_seqs; base += kWave) {
-    const int s = base + lane;
-    const int n = s < a.num_seqs ? min(clamp_len(seq_len(a, s), a.max_blocks, a.block_size), cap)
-                                 : 0;
-    const int c = s < a.num_seqs ? items_in_bucket(n, k, P) : 0;
-    int incl = c;  // inclusive prefix sum over the lanes
+  // Rounds of kOrderThreads sequences, in sequence order: within a wave a
+  // lane's rank in a bucket comes from a prefix sum (top bucket) or a
+  // ballot of the lanes sharing its bucket; waves then take consecutive
+  // ranges of each bucket.
+  for (int base = 0; base < a.num_seqs; base += kOrderThreads) {
+    if (lane < NB) wave_at[w][lane] = 0;
+    __syncthreads();
+    const int s = base + t;
+    int full = 0, top = 0, k = -1;
+    if (s < a.num_seqs) items(s, full, top, k);
+    int incl = top;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
-      const int t = __shfl_up(incl, d, kWave);
-      if (lane >= d) incl += t;
+      const int u = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += u;
     }
-    const int total = __shfl(incl, kWave - 1, kWave);
-    if (r < total) {
-      const uint64_t hit = __ballot(incl > r);
-      const int L = __ffsll((unsigned long long)hit) - 1;
-      const int before = __shfl(incl - c, L, kWave);
-      const int nl = __shfl(n, L, kWave);
-      const int within = r - before;
-      // top bucket: the full partitions 0..f-1 first, then a partial one
-      const int pt = (k == kOrderBuckets && within < nl / P) ? within : (k == 0 ? 0 : nl / P);
-      // both are wave-uniform: say so, so everything derived from them
-      // (lengths, table row, chunk bases) stays in scalar registers
-      seq = __builtin_amdgcn_readfirstlane(base + L);
-      part = __builtin_amdgcn_readfirstlane(pt);
-      return true;
+    if (lane == kWave - 1) wave_at[w][kOrderBuckets] = incl;
+    int below = 0;
+    uint64_t todo = __ballot(k >= 0);
+    while (todo) {
+      const int kk = __shfl(k, __ffsll((unsigned long long)todo) - 1, kWave);
+      const uint64_t m = __ballot(k == kk);
+      const int lower = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      if (k == kk) below = lower;
+      if (lane == 0) wave_at[w][kk] = __popcll(m);
+      todo &= ~m;
     }
-    r -= total;
+    __syncthreads();
+    if (t < NB) {
+      int run = next[t];
+      for (int v = 0; v < NW; ++v) {
+        const int c = wave_at[v][t];
+        wave_at[v][t] = run;
+        run += c;
+      }
+      next[t] = run;
+    }
+    __syncthreads();
+    int32_t* order = a.order;
+    const int pos = wave_at[w][kOrderBuckets] + incl - top;
+    for (int j = 0; j < top; ++j) order[pos + j] = (j << 12) | s;
+    if (k >= 0) order[wave_at[w][k] + below] = (full << 12) | s;
+    __syncthreads();
   }
-  return false;  // not reached: the histogram counted this item
+  for (int r = total + t; r < max_items; r += kOrderThreads) a.order[r] = -1;
 }
 
 // A work item is (sequence, group of KPW adjacent kv-heads, partition).
 // SMALL: blocks hold fewer tokens than a chunk, so each load group looks up
 // its own block; otherwise a chunk lies inside one block.
-template <int D, int G, int KPW, bool FUSED, bool SMALL>
+template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
 void decode_split_kernel(DecodeArgs a) {
   constexpr int U = unroll_for(G);
@@ -502,16 +551,18 @@ void decode_split_kernel(DecodeArgs a) {
   const int n_groups = H_kv / KPW;  // kv-head groups (the host checks divisibility)
   const int gw = blockIdx.x % n_groups;  // the kv-head groups of one item are adjacent
   int b, part;
-  if (a.ordered) {
-    // items longest first (find_item)
-    if (!find_item(a, blockIdx.x / n_groups, b, part)) return;
+  if (a.order) {
+    // items longest first (decode_order_kernel)
+    const int v = a.order[blockIdx.x / n_groups];
+    if (v < 0) return;
+    b = __builtin_amdgcn_readfirstlane(v & 4095);
+    part = __builtin_amdgcn_readfirstlane(v >> 12);
   } else {
     // highest partition first
     const int idx = blockIdx.x / n_groups;
     b = idx % a.num_seqs;
     part = a.max_parts - 1 - idx / a.num_seqs;
   }
-  __builtin_amdgcn_sched_barrier(0);  // keep the item search apart from the main loop
   const int lane = threadIdx.x;
   const int sub = lane % LPT;                 // which 8 elements of the head vector
   const int g = gw * KPW + (lane / LPT) % KPW;  // this lane's kv-head
@@ -554,44 +605,66 @@ void decode_split_kernel(DecodeArgs a) {
   // k_new/v_new instead of the cache; only [start, cend) is read from the cache.
   const int cend = (FUSED && end == n) ? n - 1 : end;
   const int nfull = (cend - start) / CHUNK;  // chunks with no token past cend
-  // Loads of full chunk i: one table lookup when the chunk lies in one
-  // block, else one per load group of TPI tokens.
-  auto issue = [&](int i, uint4 (&kr)[U], uint4 (&vr)[U]) {
-    const int cc = start + i * CHUNK;
+  // Full chunk i: its first token and the table entries of its blocks (one
+  // when the chunk lies in one block, else one per load group of TPI
+  // tokens). i is clamped to the last full chunk, so a lookup ahead never
+  // reads past the sequence's table entries. The entries are raw: the
+  // offsets are formed in issue(), so a lookup ahead does not wait for its
+  // table read.
+  struct Lookup {
+    int pos;
+    int blk[SMALL ? U : 1];
+  };
+  auto lookup = [&](int i) {
+    Lookup r;
+    r.pos = start + min(i, nfull - 1) * CHUNK;
+#pragma unroll
+    for (int u = 0; u < (SMALL ? U : 1); ++u) r.blk[u] = bt[(r.pos + u * TPI) >> a.block_shift];
+    return r;
+  };
+  auto issue = [&](const Lookup& t, uint4 (&kr)[U], uint4 (&vr)[U]) {
     if constexpr (!SMALL) {
-      const int64_t off = token_offset(a, bt, cc, row_bytes);
+      const int64_t off = block_offset(a, t.blk[0], t.pos, row_bytes);
       issue_chunk<L, U>(kc + off, vc + off, row_bytes, lane_off, kr, vr);
     } else {
       int64_t off[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) off[u] = token_offset(a, bt, cc + u * TPI, row_bytes);
+      for (int u = 0; u < U; ++u) off[u] = block_offset(a, t.blk[u], t.pos + u * TPI, row_bytes);
       issue_chunk_groups<U>(kc, vc, off, lane_off, kr, vr);
     }
   };
 #if PA_DECODE_PIPE
   // Software pipeline over two register buffers: chunk i+1's loads are in
-  // flight while chunk i is multiplied. The loop body has no branches, so
-  // the same number of loads is outstanding on every path and the
-  // compiler's memory-counter waits stay partial. The last one or two
-  // chunks are finished after the loop, so no chunk is loaded twice; with
-  // 8 q-heads that epilogue no longer fits the register file, and the loop
-  // instead runs to the end with the prefetch index clamped (the last chunk
-  // is then loaded twice).
+  // flight while chunk i is multiplied, and the table entry of chunk i+2 is
+  // read before chunk i+1's loads are issued, so it has arrived by the time
+  // it is needed (a table read right before its chunk's loads would put its
+  // latency in front of every chunk; after a drain the compiler makes table
+  // reads vector loads, which complete in order behind the chunk's loads).
+  // The loop body has no branches. The last one or two chunks are finished
+  // after the loop, so no chunk is loaded twice; with 8 q-heads that
+  // epilogue no longer fits the register file, and the loop instead runs to
+  // the end with the prefetch clamped (the last chunk is then loaded twice).
   if (nfull > 0) {
     constexpr bool kEpilogue = G < 8;
     uint4 ka[U], va[U], kb[U], vb[U];
-    issue(0, ka, va);
+    issue(lookup(0), ka, va);
+    Lookup next = lookup(1);
     int i = 0;
     for (; kEpilogue ? i + 2 < nfull : i + 2 <= nfull; i += 2) {
-      issue(i + 1, kb, vb);
+      drain_loads<U, DRAIN>();
+      const Lookup after = lookup(i + 2);
+      issue(next, kb, vb);  // chunk i+1
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the multiply
       compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
-      issue(kEpilogue ? i + 2 : min(i + 2, nfull - 1), ka, va);
+      drain_loads<U, DRAIN>();
+      next = lookup(i + 3);
+      issue(after, ka, va);  // chunk i+2 (clamped)
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
     }
     if (kEpilogue && i + 1 < nfull) {
-      issue(i + 1, kb, vb);
+      drain_loads<U, DRAIN>();
+      issue(next, kb, vb);  // chunk i+1
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
       compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
@@ -602,7 +675,7 @@ void decode_split_kernel(DecodeArgs a) {
 #else
   for (int i = 0; i < nfull; ++i) {
     uint4 kr[U], vr[U];
-    issue(i, kr, vr);
+    issue(lookup(i), kr, vr);
     compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, kr, vr);
   }
 #endif
@@ -723,21 +796,29 @@ __global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a, int 
 
 using SplitFn = void (*)(DecodeArgs);
 
-template <int D, int KPW, bool FUSED, bool SMALL>
+// DRAIN is built only where it changes the code: chunks of 8 loads (G < 8)
+// inside one block.
+template <int D, int KPW, bool FUSED, bool SMALL, bool DRAIN>
 SplitFn pick_split(int G) {
+  constexpr bool kD = DRAIN && !SMALL;
   switch (G) {
-    case 1: return decode_split_kernel<D, 1, KPW, FUSED, SMALL>;
-    case 2: return decode_split_kernel<D, 2, KPW, FUSED, SMALL>;
-    case 4: return decode_split_kernel<D, 4, KPW, FUSED, SMALL>;
-    case 8: return decode_split_kernel<D, 8, KPW, FUSED, SMALL>;
+    case 1: return decode_split_kernel<D, 1, KPW, FUSED, SMALL, kD>;
+    case 2: return decode_split_kernel<D, 2, KPW, FUSED, SMALL, kD>;
+    case 4: return decode_split_kernel<D, 4, KPW, FUSED, SMALL, kD>;
+    case 8: return decode_split_kernel<D, 8, KPW, FUSED, SMALL, false>;
   }
   return nullptr;
 }
 
+template <int D, int KPW, bool FUSED>
+SplitFn pick_split(int G, bool small, bool drain) {
+  if (small) return pick_split<D, KPW, FUSED, true, false>(G);
+  return drain ? pick_split<D, KPW, FUSED, false, true>(G) : pick_split<D, KPW, FUSED, false, false>(G);
+}
+
 template <int D, int KPW>
-SplitFn pick_split(int G, bool fused, bool small) {
-  if (fused) return small ? pick_split<D, KPW, true, true>(G) : pick_split<D, KPW, true, false>(G);
-  return small ? pick_split<D, KPW, false, true>(G) : pick_split<D, KPW, false, false>(G);
+SplitFn pick_split(int G, bool fused, bool small, bool drain) {
+  return fused ? pick_split<D, KPW, true>(G, small, drain) : pick_split<D, KPW, false>(G, small, drain);
 }
 
 #ifndef PA_DECODE_SEGMENT
@@ -761,7 +842,8 @@ constexpr int kPartUnit = 256;
 // Resident work items the split kernel keeps on an MI355X: 256 CUs x 8 waves.
 // A fixed constant (not a device query) so the workspace size is a pure
 // function of the arguments.
-constexpr int64_t kResidentItems = 256 * 8;
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kResidentItems = kComputeUnits * 8;
 
 // Longest partition (16 (multi-head waves only), 8, 4, 2 or 1 units of 256
 // tokens) whose item count still fills half the resident slots, estimating
@@ -780,9 +862,17 @@ int default_partition_blocks(const pa_desc* d, int32_t num_seqs, int32_t max_ctx
   return 1;
 }
 
+// Workspace: the partitions' (o[d], m, l) fp32 partials when a sequence can
+// span more than one partition, then the dispatch order (one int32 per
+// sequence and partition) when the grid has more items than CUs. The order
+// matters even when every item is resident at once: a CU's share of HBM
+// bandwidth is bounded, and longest first deals the long items out across
+// the CUs instead of stacking some on a few.
 struct Plan {
   int part_tokens;
   int max_parts;
+  bool ordered;
+  size_t partial_bytes;
   size_t ws_bytes;
 };
 
@@ -791,9 +881,14 @@ Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part
   Plan p;
   p.part_tokens = part_blocks * kPartUnit;
   p.max_parts = max(1, (max_ctx + p.part_tokens - 1) / p.part_tokens);
-  p.ws_bytes = p.max_parts <= 1 ? 0
-                                : (size_t)num_seqs * d->num_q_heads * p.max_parts *
-                                      (size_t)(d->head_dim + 2) * sizeof(float);
+  p.partial_bytes = p.max_parts <= 1 ? 0
+                                     : (size_t)num_seqs * d->num_q_heads * p.max_parts *
+                                           (size_t)(d->head_dim + 2) * sizeof(float);
+  const int kpw = kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
+  const int64_t ranks = (int64_t)num_seqs * p.max_parts;
+  p.ordered = num_seqs <= PA_DECODE_ORDER_MAX_SEQS &&
+              ranks * (d->num_kv_heads / kpw) > kComputeUnits;
+  p.ws_bytes = p.partial_bytes + (p.ordered ? (size_t)((ranks * 4 + 15) & ~15) : 0);
   return p;
 }
 
@@ -867,23 +962,32 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.max_parts = plan.max_parts;
   a.block_size = desc->block_size;
   a.block_shift = log2_int(desc->block_size);
-  a.ordered = num_seqs <= PA_DECODE_ORDER_MAX_SEQS;
   a.scale_log2 = scale * kLog2e;
+  a.order = plan.ordered ? (int32_t*)((char*)workspace + plan.partial_bytes) : nullptr;
 
   hipStream_t s = (hipStream_t)stream;
   const int chunk = (kWave / (D / 8 * kpw)) * unroll_for(G);  // tokens per chunk
   const bool small = desc->block_size < chunk;
   const bool fused = nt != nullptr;
+  // the wave slots are full (2 per SIMD): one chunk of loads in flight per wave
+  const bool drain = items >= kResidentItems;
   SplitFn split = nullptr;
   if (D == 128) {
-    split = kpw == 2 ? pick_split<128, 2>(G, fused, small) : pick_split<128, 1>(G, fused, small);
+    split = kpw == 2 ? pick_split<128, 2>(G, fused, small, drain)
+                     : pick_split<128, 1>(G, fused, small, drain);
   } else {
-    split = kpw == 4   ? pick_split<64, 4>(G, fused, small)
-            : kpw == 2 ? pick_split<64, 2>(G, fused, small)
-                       : pick_split<64, 1>(G, fused, small);
+    split = kpw == 4   ? pick_split<64, 4>(G, fused, small, drain)
+            : kpw == 2 ? pick_split<64, 2>(G, fused, small, drain)
+                       : pick_split<64, 1>(G, fused, small, drain);
   }
   if (!split || (D == 128 && kpw > 2))
     return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for %d kv-heads per wave", who, kpw);
+  if (plan.ordered) {
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a,
+                       num_seqs * plan.max_parts);
+    rc = launch_status(who);
+    if (rc) return rc;
+  }
   hipLaunchKernelGGL(split, dim3((unsigned)items), dim3(kWave), 0, s, a);
   rc = launch_status(who);
   if (rc) return rc;

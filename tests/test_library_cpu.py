@@ -75,6 +75,15 @@ def test_host_argument_checks_need_no_gpu(lib):
             4 * 32 * parts * (128 + 2) * 4
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4, 256, 1) == 0
     assert lib.pa_decode_workspace_size(ctypes.byref(d), 4, 256) == 0
+    # more work items (sequence x pair of kv-heads x partition) than the 256
+    # CUs: the partials plus one int32 dispatch rank per (sequence,
+    # partition), 16-byte rounded, up to 4096 sequences
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 256, 8192, 1) == \
+        256 * 32 * 32 * (128 + 2) * 4 + 256 * 32 * 4
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4096, 256, 1) == 4096 * 4
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4097, 256, 1) == 0
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 64, 256, 1) == 0  # 256 items
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 65, 256, 1) == 65 * 4 + 12
     need = lib.pa_decode_workspace_size(ctypes.byref(d), 4, 4096)
     assert need > 0
     fake = ctypes.c_void_p(0x1000)
