@@ -430,8 +430,9 @@ __device__ __forceinline__ void compute_chunk(SplitState<D, G>& st, float scale_
 // Items are ranked by length bucket (32 buckets of part_tokens/32 tokens;
 // full partitions in the top one; empty sequences, which only write zeros,
 // last), then by (sequence, partition). One workgroup ranks them before the
-// split kernel runs and writes order[rank] = (part << 12) | sequence, -1
-// past the last item; a split wave reads its one entry. (Each wave ranking
+// split kernel runs and writes order[slot] = (part << 12) | sequence, -1
+// past the last item (slot: the rank laid out by dispatch_slot); a split
+// wave reads its one entry. (Each wave ranking
 // the items itself from the lengths cost it 8-24 us: every wave read the
 // same lengths.)
 #ifndef PA_DECODE_ORDER_MAX_SEQS
@@ -444,7 +445,28 @@ __device__ __forceinline__ int len_bucket(int len, int part_tokens) {
   return 1 + (int)(((int64_t)(len - 1) * kOrderBuckets) / part_tokens);  // 1..32
 }
 
-__global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs a, int max_items) {
+#ifndef PA_DECODE_SNAKE
+#define PA_DECODE_SNAKE 1
+#endif
+
+// Where rank r goes in the dispatch order. Workgroups are dealt to the CUs
+// in launch order, a round of `round` items (one per CU) at a time; in
+// ranked order every CU would get the same place in each round, so the
+// first CU would get the longest item of every round. Odd rounds are
+// reversed, so each CU gets a long and a short item in turn.
+__device__ __forceinline__ int dispatch_slot(int r, int round, int max_items) {
+#if PA_DECODE_SNAKE
+  const int k = r / round;
+  const int start = k * round;
+  const int len = min(round, max_items - start);
+  return (k & 1) ? start + len - 1 - (r - start) : r;
+#else
+  return r;
+#endif
+}
+
+__global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs a, int max_items,
+                                                                     int round) {
   constexpr int NB = kOrderBuckets + 1;
   constexpr int NW = kOrderThreads / kWave;
   __shared__ int next[NB];           // first free rank of each bucket
@@ -524,11 +546,13 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
     __syncthreads();
     int32_t* order = a.order;
     const int pos = wave_at[w][kOrderBuckets] + incl - top;
-    for (int j = 0; j < top; ++j) order[pos + j] = (j << 12) | s;
-    if (k >= 0) order[wave_at[w][k] + below] = (full << 12) | s;
+    for (int j = 0; j < top; ++j) order[dispatch_slot(pos + j, round, max_items)] = (j << 12) | s;
+    if (k >= 0)
+      order[dispatch_slot(wave_at[w][k] + below, round, max_items)] = (full << 12) | s;
     __syncthreads();
   }
-  for (int r = total + t; r < max_items; r += kOrderThreads) a.order[r] = -1;
+  for (int r = total + t; r < max_items; r += kOrderThreads)
+    a.order[dispatch_slot(r, round, max_items)] = -1;
 }
 
 // A work item is (sequence, group of KPW adjacent kv-heads, partition).
@@ -983,8 +1007,9 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   if (!split || (D == 128 && kpw > 2))
     return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for %d kv-heads per wave", who, kpw);
   if (plan.ordered) {
+    const int round = (int)max((int64_t)1, kComputeUnits / (desc->num_kv_heads / kpw));
     hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a,
-                       num_seqs * plan.max_parts);
+                       num_seqs * plan.max_parts, round);
     rc = launch_status(who);
     if (rc) return rc;
   }
