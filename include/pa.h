@@ -323,6 +323,32 @@ const char* pa_last_error(void);
 /* Library version, "major.minor.patch". */
 const char* pa_version(void);
 
+/*
+ * pa_set_debug -- debug mode on (nonzero) or off (0); returns the previous
+ * setting. The initial setting is on when the environment variable PA_DEBUG
+ * is set to anything but "0" at the first call that consults it.
+ *
+ * In debug mode every device entry point, after its host checks, checks the
+ * device-resident preconditions its kernels rely on, and returns
+ * PA_ERR_INVALID_ARG (pa_last_error() names the first violation found)
+ * before launching anything else:
+ *   - slot_mapping: every slot in [-1, num_blocks * block_size), no slot
+ *     twice ("Nano-vLLM 源码解读 - 3. PagedAttention", §4, -1 = skip);
+ *   - lengths: 0 <= n <= the host bound (max_context_len / max_seqlen_k)
+ *     and ceil(n / block_size) <= max_blocks_per_seq;
+ *   - block tables: the entries of blocks 0 .. ceil(n / block_size) - 1 in
+ *     [0, num_blocks) (later entries are padding and never read);
+ *   - cu_seqlens_q/k: non-decreasing from 0, k_len >= q_len, q_len <=
+ *     max_seqlen_q, k_len <= max_seqlen_k; q_len == 1 for the decode rows of
+ *     pa_mixed_varlen.
+ * The checks run on the call's stream and the call waits for them (a
+ * device-to-host copy and a stream synchronisation), so debug mode is for
+ * testing: it cannot be used under graph capture, and debug calls that
+ * overlap on one device share one violation record. Outside debug mode a
+ * broken entry is only kept from causing an out-of-bounds access.
+ */
+int pa_set_debug(int on);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ EXPORTS = (
     "pa_store_kv", "pa_decode_workspace_size", "pa_decode", "pa_decode_partitioned",
     "pa_decode_step", "pa_mixed_varlen", "pa_mixed_workspace_size",
     "pa_decode_workspace_size_ex", "pa_prefill_varlen", "pa_build_metadata",
-    "pa_last_error", "pa_version",
+    "pa_last_error", "pa_version", "pa_set_debug",
     "pa_bm_create", "pa_bm_destroy", "pa_bm_chained_hash", "pa_bm_can_allocate", "pa_bm_allocate",
     "pa_bm_deallocate", "pa_bm_can_append", "pa_bm_may_append", "pa_bm_hash_blocks",
     "pa_bm_num_free", "pa_bm_free_list", "pa_bm_block_state", "pa_bm_lookup",
@@ -119,8 +119,16 @@ def load():
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
     lib.pa_version.restype = ctypes.c_char_p
+    lib.pa_set_debug.argtypes = [ctypes.c_int]
+    lib.pa_set_debug.restype = ctypes.c_int
     _LIB = lib
     return lib
+
+
+def pa_set_debug(on: bool) -> bool:
+    """Debug mode on or off (device-resident preconditions checked before
+    every launch); returns the previous setting."""
+    return bool(load().pa_set_debug(1 if on else 0))
 
 
 def _check(rc: int) -> int:

@@ -19,7 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "store_kv.hip", "decode.hip", "prefill.hip", "block_manager.cpp"]
+SOURCES = ["api.hip", "store_kv.hip", "decode.hip", "prefill.hip", "validate.hip",
+           "block_manager.cpp"]
 
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
 HIP_FLAGS = [

@@ -32,6 +32,21 @@ inline int launch_status(const char* what) {
   return PA_OK;
 }
 
+// ------------------------------------------- debug-mode checks (validate.hip)
+
+// True when debug mode is on (PA_DEBUG in the environment, or pa_set_debug).
+bool debug_enabled();
+// Each queues its check kernels on s, waits for them and returns PA_OK or
+// PA_ERR_INVALID_ARG with the first violation in the message.
+int debug_check_slots(const char* who, const int32_t* slots, int32_t n, int64_t num_slots,
+                      hipStream_t s);
+int debug_check_tables(const char* who, const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* context_lens, const int32_t* cu_k, int32_t num_seqs,
+                       int32_t max_context_len, const pa_desc* d, hipStream_t s);
+int debug_check_varlen(const char* who, const int32_t* cu_q, const int32_t* cu_k,
+                       int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                       int32_t decode_rows, hipStream_t s);
+
 // ------------------------------------------------- decode launch (decode.hip)
 
 struct NewTokens {  // the fused store's inputs (null for plain decode)

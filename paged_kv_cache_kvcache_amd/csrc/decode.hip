@@ -959,6 +959,14 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   const int kpw = kv_heads_per_wave(desc->head_dim, desc->num_q_heads, desc->num_kv_heads);
   const int64_t items = (int64_t)num_seqs * (desc->num_kv_heads / kpw) * plan.max_parts;
   if (items > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "%s: grid too large", who);
+  if (debug_enabled()) {
+    rc = debug_check_tables(who, block_tables, max_blocks_per_seq, context_lens, cu_k, num_seqs,
+                            max_context_len, desc, (hipStream_t)stream);
+    if (!rc && nt)
+      rc = debug_check_slots(who, nt->slot_mapping, num_seqs,
+                             desc->num_blocks * desc->block_size, (hipStream_t)stream);
+    if (rc) return rc;
+  }
 
   DecodeArgs a;
   a.q = (const uint16_t*)q;

@@ -433,7 +433,7 @@ int launch_prefill(const char* who, const void* q, const void* k_cache, const vo
                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_seqs,
                    int32_t max_seqlen_q, int32_t max_seqlen_k, const int32_t* block_tables,
                    int32_t max_blocks_per_seq, float scale, void* out, const pa_desc* desc,
-                   void* stream) {
+                   void* stream, bool debug_varlen) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_blocks_per_seq < 0)
@@ -449,6 +449,17 @@ int launch_prefill(const char* who, const void* q, const void* k_cache, const vo
                 max_seqlen_k, max_blocks_per_seq);
   if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15u)
     return fail(PA_ERR_INVALID_ARG, "%s: q, caches and out must be 16-byte aligned", who);
+  if (debug_enabled()) {
+    // debug_varlen: the batch is the caller's whole cu_seqlens (else a mixed
+    // batch's prefill rows, whose prefix sums were checked as a whole)
+    if (debug_varlen)
+      rc = debug_check_varlen(who, cu_seqlens_q, cu_seqlens_k, num_seqs, max_seqlen_q,
+                              max_seqlen_k, 0, (hipStream_t)stream);
+    if (!rc)
+      rc = debug_check_tables(who, block_tables, max_blocks_per_seq, nullptr, cu_seqlens_k,
+                              num_seqs, max_seqlen_k, desc, (hipStream_t)stream);
+    if (rc) return rc;
+  }
   const int G = desc->num_q_heads / desc->num_kv_heads;
   const int D = desc->head_dim;
   const int QB = kCols / G;
@@ -489,7 +500,7 @@ extern "C" int pa_prefill_varlen(const void* q, const void* k_cache, const void*
                                  float scale, void* out, const pa_desc* desc, void* stream) {
   return pa::launch_prefill("pa_prefill_varlen", q, k_cache, v_cache, cu_seqlens_q,
                             cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, block_tables,
-                            max_blocks_per_seq, scale, out, desc, stream);
+                            max_blocks_per_seq, scale, out, desc, stream, true);
 }
 
 extern "C" size_t pa_mixed_workspace_size(const pa_desc* desc, int32_t num_decode_rows,
@@ -513,6 +524,12 @@ extern "C" int pa_mixed_varlen(const void* q, const void* k_cache, const void* v
   if (num_decode_rows < 0 || num_decode_rows > num_seqs)
     return fail(PA_ERR_INVALID_ARG, "pa_mixed_varlen: num_decode_rows %d outside [0, %d]",
                 num_decode_rows, num_seqs);
+  if (debug_enabled() && num_seqs > 0 && cu_seqlens_q && cu_seqlens_k) {
+    // the prefix sums as a whole; each launch below checks its rows' tables
+    rc = debug_check_varlen("pa_mixed_varlen", cu_seqlens_q, cu_seqlens_k, num_seqs,
+                            max_seqlen_q, max_seqlen_k, num_decode_rows, (hipStream_t)stream);
+    if (rc) return rc;
+  }
   if (num_decode_rows > 0) {
     rc = launch_decode("pa_mixed_varlen", q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                        nullptr, cu_seqlens_k, num_decode_rows, max_seqlen_k, scale, out,
@@ -526,7 +543,7 @@ extern "C" int pa_mixed_varlen(const void* q, const void* k_cache, const void* v
     rc = launch_prefill("pa_mixed_varlen", q, k_cache, v_cache, cu_seqlens_q + num_decode_rows,
                         cu_seqlens_k + num_decode_rows, rest, max_seqlen_q, max_seqlen_k,
                         block_tables + (int64_t)num_decode_rows * max_blocks_per_seq,
-                        max_blocks_per_seq, scale, out, desc, stream);
+                        max_blocks_per_seq, scale, out, desc, stream, false);
   }
   return rc;
 }

@@ -74,6 +74,10 @@ extern "C" int pa_store_kv(const void* k, int64_t k_row_stride, const void* v,
                 (long long)k_row_stride, (long long)v_row_stride, row);
   const int64_t num_slots = desc->num_blocks * desc->block_size;
   hipStream_t s = (hipStream_t)stream;
+  if (debug_enabled()) {
+    rc = debug_check_slots("pa_store_kv", slot_mapping, n_tokens, num_slots, s);
+    if (rc) return rc;
+  }
   const bool vec = aligned16(k) && aligned16(v) && aligned16(k_cache) && aligned16(v_cache) &&
                    (k_row_stride % 8 == 0) && (v_row_stride % 8 == 0) && (row % 8 == 0);
   if (vec) {

@@ -142,3 +142,20 @@ def test_metadata_rejects_padding_and_bad_ranges(lib):
         B.pa_build_metadata(tables, [5], [2], 256)
     with pytest.raises(B.PAError):
         B.pa_build_metadata(tables, [0], [600], 256)  # needs 3 blocks, table has 2
+
+
+def test_debug_switch_needs_no_gpu(lib):
+    prev = lib.pa_set_debug(1)
+    try:
+        assert lib.pa_set_debug(1) == 1
+        d = _desc()
+        # host checks and no-op calls come first: nothing reaches the device
+        assert lib.pa_store_kv(None, 0, None, 0, None, None, None, 0, ctypes.byref(d), None) == 0
+        assert lib.pa_store_kv(None, 0, None, 0, None, None, None, 4, ctypes.byref(d), None) == \
+            B.PA_ERR_INVALID_ARG
+        assert lib.pa_decode(None, None, None, None, 0, None, 0, 0, 1.0, None, None, 0,
+                             ctypes.byref(d), None) == 0
+        assert lib.pa_set_debug(0) == 1
+        assert lib.pa_set_debug(0) == 0
+    finally:
+        lib.pa_set_debug(prev)
