@@ -83,31 +83,71 @@ def traffic_from_profile(pmc_file: str, kernel_src: str, mode: str | None,
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(case, budget_s: float):
-    """The fp64 oracle on the host, one thread, over the first sequences of
-    the same batch until about ``budget_s`` seconds are spent."""
-    import numpy as np
+def _oracle_rows(rows):
+    """Worker: the oracle's decode of the given sequences of the inherited case."""
+    import oracle
+    c = _CPU_CASE
+    for b in rows:
+        oracle.decode_one(c.q[b], c.k_cache, c.v_cache, c.block_tables[b], int(c.context_lens[b]),
+                          c.scale)
+    return len(rows)
+
+
+_CPU_CASE = None
+
+
+def cpu_baseline_child(args) -> int:
+    """Runs in a fresh interpreter that never touches the GPU: draws the same
+    workload and times the fp64 oracle's decode of its sequences in a pool of
+    worker processes, one per host core (at most 16, one thread each), until
+    the batch is done or about ``--cpu-budget`` seconds have passed."""
+    import multiprocessing as mp
+
     from threadpoolctl import threadpool_limits
 
-    import oracle
-    done, tokens = 0, 0
-    t0 = time.perf_counter()
+    from paged_kv_cache_kvcache_amd import workloads as W
+    global _CPU_CASE
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    case = W.make_case(args.config, block_size=args.block_size, threads=cores)
+    _CPU_CASE = case
+    chunks = [list(range(b, min(b + 4, case.batch))) for b in range(0, case.batch, 4)]
+    done = 0
     with threadpool_limits(1):
-        for b in range(case.batch):
-            oracle.decode_one(case.q[b], case.k_cache, case.v_cache, case.block_tables[b],
-                              int(case.context_lens[b]), case.scale)
-            done += 1
-            tokens += int(case.context_lens[b])
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    el = time.perf_counter() - t0
+        pool = mp.get_context("fork").Pool(cores)
+        try:
+            t0 = time.perf_counter()
+            for n in pool.imap(_oracle_rows, chunks):
+                done += n
+                if time.perf_counter() - t0 >= args.cpu_budget:
+                    break
+            el = time.perf_counter() - t0
+        finally:
+            pool.terminate()
+    tokens = int(case.context_lens[:done].sum())
     kv = tokens * case.num_kv_heads * case.head_dim * 2 * 2
     qo = 2 * done * case.num_q_heads * case.head_dim * 2
-    return {"value": round((kv + qo) / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "fp64 numpy oracle decode of the first %d of %d sequences (%d context "
-                      "tokens, %.1f s, 1 thread); store not included" % (
-                          done, case.batch, tokens, el),
-            "tokens_per_s_per_layer": round(done / el, 3)}
+    print(json.dumps({
+        "value": round((kv + qo) / el / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": "fp64 numpy oracle decode of the first %d of %d sequences (%d context tokens) "
+                  "in %d worker processes of one thread each, %.2f s; store not included" % (
+                      done, case.batch, tokens, cores, el),
+        "tokens_per_s_per_layer": round(done / el, 3)}), flush=True)
+    return 0
+
+
+def cpu_baseline(args):
+    """The CPU oracle baseline, measured in a child process (see
+    cpu_baseline_child) so that its workers fork from a process without a
+    GPU context."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--config",
+           args.config, "--block-size", str(args.block_size), "--cpu-budget",
+           str(args.cpu_budget)]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True,
+                       timeout=args.cpu_budget + 600)
+    if r.returncode != 0:
+        raise RuntimeError("CPU baseline failed (%d): %s" % (r.returncode, r.stderr[-2000:]))
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 def run_prefill(args, torch, B, W, dev):
@@ -247,7 +287,10 @@ def main() -> int:
                     help="tokens per cache block (power of two, 16..1024); same lengths")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_baseline_child:
+        return cpu_baseline_child(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -418,7 +461,7 @@ def main() -> int:
     if args.mixed:
         rec["mixed"] = run_mixed(args, torch, B, W, dev)
     if args.cpu_budget > 0:
-        rec["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+        rec["cpu_baseline"] = cpu_baseline(args)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

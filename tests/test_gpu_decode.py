@@ -186,17 +186,22 @@ def test_prefill_store_bit_exact():
     assert np.array_equal(host_bits(kc), kref) and np.array_equal(host_bits(vc), vref)
 
 
-def test_large_batch_of_short_sequences_plain_order():
-    """Over 1,024 sequences the split kernel keeps the plain dispatch order
-    (highest partition first) instead of ranking items by length; lengths
-    1..600 with a few padding rows, sampled rows and every padding row vs
-    the oracle."""
-    rng = np.random.default_rng(77)
-    lens = rng.integers(1, 600 + 1, size=1536)
-    lens[[3, 700, 1535]] = 0
-    case = W.decode_case(32, 8, 128, lens, seed=78)
+@pytest.mark.parametrize("batch,h_q,h_kv,d", [(1536, 32, 8, 128), (4096, 8, 2, 64),
+                                              (4097, 8, 2, 64)])
+def test_large_batch_of_short_sequences(batch, h_q, h_kv, d):
+    """Large batches of short sequences: up to 4,096 sequences the items are
+    ranked by the order kernel (sequence ids fill its 12 bits at 4,096), one
+    more keeps the plain dispatch order (highest partition first). Lengths
+    1..600 with a few padding rows; sampled rows and every padding row vs the
+    oracle."""
+    rng = np.random.default_rng(77 + batch)
+    lens = rng.integers(1, 600 + 1, size=batch)
+    pad = [3, 700, batch - 1]
+    lens[pad] = 0
+    case = W.decode_case(h_q, h_kv, d, lens, seed=78)
     out, caches, slots, before = run_decode_step(case)
     kc_ref, vc_ref = check_store(case, caches, slots, before)
-    rows = sorted(set(rng.choice(len(lens), 40, replace=False).tolist()) | {3, 700, 1535})
+    rows = sorted(set(rng.choice(len(lens), 40, replace=False).tolist()) | set(pad) |
+                  {batch - 2, 4095 if batch > 4095 else 0})
     check_decode(case, out, kc_ref, vc_ref, rows=rows)
-    assert np.all(out[[3, 700, 1535]] == 0)
+    assert np.all(out[pad] == 0)
