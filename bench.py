@@ -63,8 +63,15 @@ def prefill_flops(starts, ends, h_q: int, d: int) -> float:
 
 
 def src_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of a kernel source's code: `//` comments and blank space are
+    left out, so a comment edit does not retire counters taken on the same
+    code."""
+    import re
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    code = "\n".join(" ".join(re.sub(r"//.*", "", line).split()) for line in text.splitlines())
+    code = re.sub(r"\n+", "\n", code).strip()
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_from_profile(pmc_file: str, kernel_src: str, mode: str | None,

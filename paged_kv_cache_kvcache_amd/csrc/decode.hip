@@ -14,10 +14,10 @@
 //     unnormalised output) triples exactly. Sequences that fit one
 //     partition are finished by the first kernel.
 //   * dispatch: when the grid has more items than CUs, a one-workgroup
-//     kernel first ranks them longest first, so long items are spread over
-//     the CUs and the bandwidth-bound grid drains on short ones; batches of
-//     more than 4,096 sequences keep the plain order (highest partition
-//     first).
+//     kernel first ranks them longest first and lays the ranks out so each
+//     CU gets long and short items in turn; the bandwidth-bound grid then
+//     drains on short items. Batches of more than 4,096 sequences keep the
+//     plain order (highest partition first).
 //   * loads in flight: at full occupancy a wave waits for a chunk's loads
 //     before issuing the next chunk's; with fewer waves two chunks overlap
 //     (the host picks the kernel).
@@ -25,9 +25,10 @@
 //     serves G heads.
 //   * loads: 16 bytes per lane, nontemporal (K/V are read once); d/8 lanes
 //     cover one kv-head vector and KPW adjacent kv-heads make a 512-byte
-//     contiguous piece of a token row. Eight loads of K and eight of V are
-//     in flight per wave, and the next chunk's loads are issued before the
-//     current chunk is multiplied (two register buffers).
+//     contiguous piece of a token row. A chunk is eight loads of K and
+//     eight of V (four with 8 q-heads per kv-head), and the next chunk's
+//     loads are issued before the current chunk is multiplied (two register
+//     buffers; block-table entries are read two chunks ahead).
 //   * q.k: v_dot2_f32_bf16 on the raw bf16 pairs (exact products, fp32 sum),
 //     then DPP exchanges (no LDS); at d = 128 a transposed butterfly leaves
 //     each lane with one token's full score.
