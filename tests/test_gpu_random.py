@@ -33,7 +33,7 @@ def _shape(rng):
     return g * h_kv, h_kv, d, bsz
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_decode(seed):
     rng = np.random.default_rng(5000 + seed)
     h_q, h_kv, d, bsz = _shape(rng)
@@ -72,7 +72,7 @@ def test_random_decode(seed):
     print("  max abs %.3g mean abs %.3g" % (mx, mean), flush=True)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_prefill(seed):
     rng = np.random.default_rng(7000 + seed)
     h_q, h_kv, d, bsz = _shape(rng)
