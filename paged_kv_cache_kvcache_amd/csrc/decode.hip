@@ -172,10 +172,10 @@ __device__ __forceinline__ uint4 load16(const char* p) {
 // has one chunk of loads in flight while it multiplies the chunk before.
 // Without the wait the compiler's partial waits inside the multiply let two
 // chunks' loads overlap. With every wave slot of the chip filled, the
-// overlap only adds requests to already full memory queues (measured 3%
-// slower); with fewer waves it is what keeps enough bytes in flight
-// (without it, up to twice as slow at one wave per SIMD), so the host
-// picks the kernel. Chunks of 4 loads never wait here.
+// overlap only adds requests to already full memory queues (measured 5%
+// slower at the Qwen3-8B batch); with fewer waves it is what keeps enough
+// bytes in flight (waiting here measured up to twice as slow at one wave
+// per SIMD), so the host picks the kernel. Chunks of 4 loads never wait.
 template <int U, bool DRAIN>
 __device__ __forceinline__ void drain_loads() {
 #if PA_DECODE_DRAIN
