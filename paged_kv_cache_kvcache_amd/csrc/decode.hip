@@ -542,8 +542,11 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
 // A work item is (sequence, group of KPW adjacent kv-heads, partition).
 // SMALL: blocks hold fewer tokens than a chunk, so each load group looks up
 // its own block; otherwise a chunk lies inside one block.
-template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
+// VS waves per workgroup share a kv-head, each with G of its q-heads (VS = 2
+// at 16 q-heads per kv-head: a wave holds at most 8); they read the same
+// K/V rows on the same CU, so the second read is served by its caches.
+template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1>
+__global__ __launch_bounds__(kWave * VS) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
 void decode_split_kernel(DecodeArgs a) {
   constexpr int U = unroll_for(G);
   using S = SplitState<D, G>;
@@ -555,7 +558,7 @@ void decode_split_kernel(DecodeArgs a) {
   static_assert(kMinBlockSize % TPI == 0, "a load group never straddles a block");
 
   const int H_kv = a.num_kv_heads;
-  const int H_q = H_kv * G;
+  const int H_q = H_kv * G * VS;
   const int n_groups = H_kv / KPW;  // kv-head groups (the host checks divisibility)
   const int gw = blockIdx.x % n_groups;  // the kv-head groups of one item are adjacent
   int b, part;
@@ -571,14 +574,15 @@ void decode_split_kernel(DecodeArgs a) {
     b = idx % a.num_seqs;
     part = a.max_parts - 1 - idx / a.num_seqs;
   }
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int half = VS == 1 ? 0 : threadIdx.x / kWave;  // which G q-heads of the kv-head
   const int sub = lane % LPT;                 // which 8 elements of the head vector
   const int g = gw * KPW + (lane / LPT) % KPW;  // this lane's kv-head
   const int row = lane / SEG;                 // which token of a load instruction
 
   const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
   const Parts parts = split_parts(n, a.part_tokens, a.max_parts);
-  const int64_t head0 = (int64_t)b * H_q + (int64_t)g * G;  // first q-head of the group
+  const int64_t head0 = (int64_t)b * H_q + (int64_t)g * G * VS + half * G;  // first q-head
 
   if (n == 0) {  // padding row: defined as zeros, nothing read
     if (part == 0 && row == 0) {
@@ -710,7 +714,7 @@ void decode_split_kernel(DecodeArgs a) {
     const uint4 vr1[1] = {vt};
     compute_chunk<L, D, G, 1, true>(st, a.scale_log2, row, 1, kr1, vr1);
     const int slot = a.slot_mapping[b];
-    if (row == 0 && slot >= 0 && slot < (a.num_blocks << a.block_shift)) {
+    if (row == 0 && half == 0 && slot >= 0 && slot < (a.num_blocks << a.block_shift)) {
       const int64_t dst = (int64_t)slot * H_kv * D + g * D + sub * 8;
       *reinterpret_cast<uint4*>(a.k_cache_w + dst) = kt;
       *reinterpret_cast<uint4*>(a.v_cache_w + dst) = vt;
@@ -814,6 +818,9 @@ SplitFn pick_split(int G) {
     case 2: return decode_split_kernel<D, 2, KPW, FUSED, SMALL, kD>;
     case 4: return decode_split_kernel<D, 4, KPW, FUSED, SMALL, kD>;
     case 8: return decode_split_kernel<D, 8, KPW, FUSED, SMALL, false>;
+    case 16:
+      if constexpr (KPW == 1) return decode_split_kernel<D, 8, 1, FUSED, SMALL, false, 2>;
+      return nullptr;
   }
   return nullptr;
 }
@@ -838,10 +845,21 @@ SplitFn pick_split(int G, bool fused, bool small, bool drain) {
 // 7% faster than 256-byte ones), when the head count allows it; else one.
 // With 8 q-heads per kv-head the wave's arithmetic per byte is highest and
 // its chunks are shortest; there one kv-head per wave measures faster.
+// Waves per kv-head: a wave holds at most 8 q-heads, so 16 q-heads per
+// kv-head take two waves of one workgroup.
+int kv_split(const pa_desc* d) { return d->num_q_heads / d->num_kv_heads > 8 ? 2 : 1; }
+
+// Work-item groups per sequence: kv-heads over kv-heads per wave.
+int item_groups(const pa_desc* d);
+
 int kv_heads_per_wave(int head_dim, int num_q_heads, int num_kv_heads) {
   if (num_q_heads / num_kv_heads >= 8) return 1;
   const int want = PA_DECODE_SEGMENT / (2 * head_dim);
   return (want > 1 && num_kv_heads % want == 0) ? want : 1;
+}
+
+int item_groups(const pa_desc* d) {
+  return d->num_kv_heads / kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
 }
 
 // Partition lengths are counted in units of 256 tokens, whatever the block size.
@@ -862,7 +880,7 @@ constexpr int64_t kResidentItems = kComputeUnits * 8;
 int default_partition_blocks(const pa_desc* d, int32_t num_seqs, int32_t max_ctx) {
   const int64_t mean_ctx = max(1, max_ctx / 2);
   const int kpw = kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
-  const int groups = d->num_kv_heads / kpw;
+  const int groups = item_groups(d);
   for (int p = kpw > 1 ? 16 : 8; p > 1; p >>= 1) {
     const int64_t per_seq = (mean_ctx + (int64_t)p * kPartUnit - 1) / ((int64_t)p * kPartUnit);
     if ((int64_t)num_seqs * groups * per_seq >= kResidentItems / 2) return p;
@@ -892,10 +910,8 @@ Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part
   p.partial_bytes = p.max_parts <= 1 ? 0
                                      : (size_t)num_seqs * d->num_q_heads * p.max_parts *
                                            (size_t)(d->head_dim + 2) * sizeof(float);
-  const int kpw = kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
   const int64_t ranks = (int64_t)num_seqs * p.max_parts;
-  p.ordered = num_seqs <= PA_DECODE_ORDER_MAX_SEQS &&
-              ranks * (d->num_kv_heads / kpw) > kComputeUnits;
+  p.ordered = num_seqs <= PA_DECODE_ORDER_MAX_SEQS && ranks * item_groups(d) > kComputeUnits;
   p.ws_bytes = p.partial_bytes + (p.ordered ? (size_t)((ranks * 4 + 15) & ~15) : 0);
   return p;
 }
@@ -941,7 +957,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
       return fail(PA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", who);
   }
   const int kpw = kv_heads_per_wave(desc->head_dim, desc->num_q_heads, desc->num_kv_heads);
-  const int64_t items = (int64_t)num_seqs * (desc->num_kv_heads / kpw) * plan.max_parts;
+  const int64_t items = (int64_t)num_seqs * item_groups(desc) * plan.max_parts;
   if (items > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "%s: grid too large", who);
   if (debug_enabled()) {
     rc = debug_check_tables(who, block_tables, max_blocks_per_seq, context_lens, cu_k, num_seqs,
@@ -982,7 +998,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.order = plan.ordered ? (int32_t*)((char*)workspace + plan.partial_bytes) : nullptr;
 
   hipStream_t s = (hipStream_t)stream;
-  const int chunk = (kWave / (D / 8 * kpw)) * unroll_for(G);  // tokens per chunk
+  const int chunk = (kWave / (D / 8 * kpw)) * unroll_for(min(G, 8));  // tokens per chunk
   const bool small = desc->block_size < chunk;
   const bool fused = nt != nullptr;
   // the wave slots are full (2 per SIMD): one chunk of loads in flight per wave
@@ -999,13 +1015,13 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   if (!split || (D == 128 && kpw > 2))
     return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for %d kv-heads per wave", who, kpw);
   if (plan.ordered) {
-    const int round = (int)max((int64_t)1, kComputeUnits / (desc->num_kv_heads / kpw));
+    const int round = (int)max((int64_t)1, kComputeUnits / item_groups(desc));
     hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a,
                        num_seqs * plan.max_parts, round);
     rc = launch_status(who);
     if (rc) return rc;
   }
-  hipLaunchKernelGGL(split, dim3((unsigned)items), dim3(kWave), 0, s, a);
+  hipLaunchKernelGGL(split, dim3((unsigned)items), dim3(kWave * kv_split(desc)), 0, s, a);
   rc = launch_status(who);
   if (rc) return rc;
   if (plan.max_parts > 1) {

@@ -419,6 +419,7 @@ PrefillFn pick(int G) {
     case 2: return prefill_kernel<D, 2, SMALL>;
     case 4: return prefill_kernel<D, 4, SMALL>;
     case 8: return prefill_kernel<D, 8, SMALL>;
+    case 16: return prefill_kernel<D, 16, SMALL>;
   }
   return nullptr;
 }

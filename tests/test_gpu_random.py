@@ -27,7 +27,7 @@ def _gpu():
 
 def _shape(rng):
     d = int(rng.choice([64, 128]))
-    g = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
     h_kv = int(rng.choice([1, 2, 3, 4, 8]))
     bsz = int(rng.choice([16, 32, 64, 128, 256, 512, 1024]))
     return g * h_kv, h_kv, d, bsz
