@@ -37,7 +37,14 @@
 //     once at the end.
 //   * P.V: weights rounded to bf16 pairs, v_dot2_f32_bf16 on paired V rows,
 //     fp32 accumulation; the sum adds the same rounded weights.
+//   * 8 or 16 q-heads per kv-head at d = 128: the vector work per byte grows
+//     with the group and would bound the kernel, so both products run on
+//     the matrix cores instead (v_mfma_f32_16x16x32_bf16, the q-heads as
+//     the 16 columns), with each chunk's K rows and V^T staged through a
+//     per-wave LDS region (compute_chunk_mf). Loads, pipeline and dispatch
+//     are the same.
 #include <cmath>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -359,7 +366,7 @@ __device__ __forceinline__ void compute_chunk_t(SplitState<D, G>& st, float scal
 }
 
 template <class S, int D, int G, int U, bool TAIL>
-__device__ __forceinline__ void compute_chunk(SplitState<D, G>& st, float scale_log2, int row,
+__device__ __forceinline__ void compute_chunk_v(SplitState<D, G>& st, float scale_log2, int row,
                                               int nvalid, const uint4 (&kr)[U],
                                               const uint4 (&vr)[U]) {
   if constexpr (PA_DECODE_TRANSPOSE && S::LPT == 16 && (U == 4 || U == 8)) {
@@ -437,6 +444,163 @@ __device__ __forceinline__ void compute_chunk(SplitState<D, G>& st, float scale_
       for (int e = 0; e < 8; ++e) st.acc[h][e] = fmaf(p, vf[e], st.acc[h][e]);
     }
   }
+  }
+}
+
+// ---- matrix-core variant (d = 128, one kv-head per wave, up to 16 q-heads)
+//
+// The chunk's 32 tokens go through a per-wave LDS region so that both
+// products run on v_mfma_f32_16x16x32_bf16 with the q-heads as the 16
+// columns: S^T = K Q^T, then O^T += V^T P^T. Lane (g, i) = (lane / 16,
+// lane % 16) loaded token 4u + g, elements 8i .. 8i+7, for u = 0..7. K row
+// 4g + (u & 3) of 16-token tile u >> 2 holds that token, so the S^T
+// accumulator of tile T gives lane (g, i), register c, the score of q-head i
+// for token 16T + 4c + g. Numbered that way, the 8 scores a lane holds are
+// the 8 keys of its lane group in the B operand of the P.V product, and V^T
+// is staged in the same key order (slot 8g + u holds token 4u + g), so P
+// stays in registers. Columns past G carry zero queries and are never
+// written.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+struct MfState {
+  bf16x8 qf[4];  // Q^T operand of k-step j: lane (g, i) = q-head i, elements 32j + 8g ..
+  f32x4 o[8];    // O^T tile mt: lane (g, i), register c = element 16mt + 4g + c of q-head i
+  float m;       // column i's running max (log2 units); equal in the column's 4 lanes
+  float l;       // this lane's share of column i's sum (its tokens only)
+};
+
+constexpr int kMfKBytes = 2 * 16 * 256;         // two 16-token K tiles, 256-byte rows
+constexpr int kMfVRow = 80;                      // V^T row: 32 keys x 2 B, padded
+constexpr int kMfBytes = kMfKBytes + 128 * kMfVRow;  // LDS per wave
+// A column's reference max moves only when a score exceeds it by more than
+// 2^kMfLazy (weights stay <= 256, exact in the fp32 sums).
+constexpr float kMfLazy = 8.f;
+
+__device__ __forceinline__ float sum_pair_bf16(uint32_t pair, float acc) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                         __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
+}
+
+// LDS rows are swizzled so that every access below is free of bank
+// conflicts: K block b of row rho sits at b ^ rho; the V^T 16-byte group of
+// lane group g in row d sits at g ^ ((d >> 4) & 3).
+template <bool TAIL>
+__device__ __forceinline__ void compute_chunk_mf(MfState& st, char* lds, float scale_log2,
+                                                 int nvalid, const uint4 (&kr)[8],
+                                                 const uint4 (&vr)[8]) {
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, i = lane & 15;
+  char* vt = lds + kMfKBytes;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int rho = 4 * g + (u & 3);
+    *reinterpret_cast<uint4*>(lds + (u >> 2) * 4096 + rho * 256 + ((i ^ rho) << 4)) = kr[u];
+  }
+  // V^T: dword k of the lane's group holds tokens u = 2k (low) and 2k + 1
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t x4[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+      c[u] = x4[w];
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t sel = e ? 0x07060302u : 0x05040100u;  // element 2w + e of both tokens
+      uint4 x;
+      x.x = __builtin_amdgcn_perm(c[1], c[0], sel);
+      x.y = __builtin_amdgcn_perm(c[3], c[2], sel);
+      x.z = __builtin_amdgcn_perm(c[5], c[4], sel);
+      x.w = __builtin_amdgcn_perm(c[7], c[6], sel);
+      const int d = 8 * i + 2 * w + e;
+      *reinterpret_cast<uint4*>(vt + d * kMfVRow + ((g ^ ((d >> 4) & 3)) << 4)) = x;
+    }
+  }
+  // a wave's LDS operations execute in order: only the compiler must keep
+  // the reads below after the writes above
+  asm volatile("" ::: "memory");
+  f32x4 sc[2];
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    sc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 av = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(lds + T * 4096 + i * 256 + (((4 * j + g) ^ i) << 4)));
+      sc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, st.qf[j], sc[T], 0, 0, 0);
+    }
+  }
+  float sv[8];  // token 16T + 4c + g at index 4T + c
+#pragma unroll
+  for (int T = 0; T < 2; ++T)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float x = sc[T][c];
+      sv[4 * T + c] = (!TAIL || 16 * T + 4 * c + g < nvalid) ? x : -INFINITY;
+    }
+  float mx = sv[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) mx = fmaxf(mx, sv[k]);
+  mx = fmaxf(mx, xor_lane(mx, 16));
+  mx = fmaxf(mx, xor_lane(mx, 32));
+  mx *= scale_log2;  // scale > 0 commutes with max
+  if (mx > st.m + kMfLazy) {  // the column's 4 lanes agree
+    const float mnew = fmaxf(st.m, mx);
+    const float alpha = fast_exp2(st.m - mnew);  // 0 on the first chunk
+    st.m = mnew;
+    st.l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) st.o[mt] *= alpha;
+  }
+  const float negm = (st.m == -INFINITY) ? 0.f : -st.m;
+  float p[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) p[k] = fast_exp2(fmaf(sv[k], scale_log2, negm));
+  uint4 pk;
+  pk.x = pack2_bf16_hw(p[0], p[1]);
+  pk.y = pack2_bf16_hw(p[2], p[3]);
+  pk.z = pack2_bf16_hw(p[4], p[5]);
+  pk.w = pack2_bf16_hw(p[6], p[7]);
+  // the sum adds the rounded weights the products see (an exact weighted mean)
+  st.l = sum_pair_bf16(pk.x, st.l);
+  st.l = sum_pair_bf16(pk.y, st.l);
+  st.l = sum_pair_bf16(pk.z, st.l);
+  st.l = sum_pair_bf16(pk.w, st.l);
+  const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+    const int d = 16 * mt + i;
+    const bf16x8 av = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const uint4*>(vt + d * kMfVRow + ((g ^ (mt & 3)) << 4)));
+    st.o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf, st.o[mt], 0, 0, 0);
+  }
+  // the next chunk's LDS writes stay after these reads
+  asm volatile("" ::: "memory");
+}
+
+// One chunk on either path: the matrix-core state takes U = 8 (a single
+// fused token is widened to a masked chunk of 8 copies).
+template <class L, int D, int G, int U, bool TAIL, class St>
+__device__ __forceinline__ void compute_chunk(St& st, char* lds, float scale_log2, int row,
+                                              int nvalid, const uint4 (&kr)[U],
+                                              const uint4 (&vr)[U]) {
+  if constexpr (std::is_same<St, MfState>::value) {
+    if constexpr (U == 8) {
+      compute_chunk_mf<TAIL>(st, lds, scale_log2, nvalid, kr, vr);
+    } else {
+      uint4 k8[8], v8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        k8[u] = kr[u % U];
+        v8[u] = vr[u % U];
+      }
+      compute_chunk_mf<true>(st, lds, scale_log2, nvalid, k8, v8);
+    }
+  } else {
+    compute_chunk_v<L, D, G, U, TAIL>(st, scale_log2, row, nvalid, kr, vr);
   }
 }
 
@@ -545,11 +709,13 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
 // VS waves per workgroup share a kv-head, each with G of its q-heads (VS = 2
 // at 16 q-heads per kv-head: a wave holds at most 8); they read the same
 // K/V rows on the same CU, so the second read is served by its caches.
-template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1>
+// MF: the matrix-core variant (d = 128, KPW = 1, VS = 1, G <= 16).
+template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1, bool MF = false>
 __global__ __launch_bounds__(kWave * VS) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
 void decode_split_kernel(DecodeArgs a) {
-  constexpr int U = unroll_for(G);
-  using S = SplitState<D, G>;
+  static_assert(!MF || (D == 128 && KPW == 1 && VS == 1 && G <= 16), "matrix-core geometry");
+  constexpr int U = MF ? 8 : unroll_for(G);
+  using S = typename std::conditional<MF, MfState, SplitState<D, G>>::type;
   using L = Lanes<D, KPW>;
   constexpr int LPT = L::LPT;
   constexpr int SEG = L::SEG;
@@ -598,14 +764,32 @@ void decode_split_kernel(DecodeArgs a) {
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
 
   S st;
+  char* lds = nullptr;
+  if constexpr (MF) {
+    __shared__ __attribute__((aligned(16))) char mf_lds[kMfBytes];
+    lds = mf_lds;
+    // lane (g, i): q-head i (zeros past G), elements 32j + 8g .. +8
+    const int qg = lane >> 4, qi = lane & 15;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 t = *reinterpret_cast<const uint4*>(a.q + (head0 + h) * D + sub * 8);
-    st.qv[h][0] = t.x; st.qv[h][1] = t.y; st.qv[h][2] = t.z; st.qv[h][3] = t.w;
-    st.m[h] = -INFINITY;
-    st.l[h] = 0.f;
+    for (int j = 0; j < 4; ++j) {
+      uint4 t = make_uint4(0, 0, 0, 0);
+      if (qi < G) t = *reinterpret_cast<const uint4*>(a.q + (head0 + qi) * D + 32 * j + 8 * qg);
+      st.qf[j] = __builtin_bit_cast(bf16x8, t);
+    }
+    st.m = -INFINITY;
+    st.l = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
+    for (int mt = 0; mt < 8; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint4 t = *reinterpret_cast<const uint4*>(a.q + (head0 + h) * D + sub * 8);
+      st.qv[h][0] = t.x; st.qv[h][1] = t.y; st.qv[h][2] = t.z; st.qv[h][3] = t.w;
+      st.m[h] = -INFINITY;
+      st.l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
+    }
   }
 
   const int64_t row_bytes = (int64_t)H_kv * D * 2;  // bytes per token row of a cache
@@ -653,11 +837,12 @@ void decode_split_kernel(DecodeArgs a) {
   // latency in front of every chunk; after a drain the compiler makes table
   // reads vector loads, which complete in order behind the chunk's loads).
   // The loop body has no branches. The last one or two chunks are finished
-  // after the loop, so no chunk is loaded twice; with 8 q-heads that
-  // epilogue no longer fits the register file, and the loop instead runs to
-  // the end with the prefetch clamped (the last chunk is then loaded twice).
+  // after the loop, so no chunk is loaded twice; with 8 q-heads on the
+  // vector path that epilogue no longer fits the register file, and the loop
+  // instead runs to the end with the prefetch clamped (the last chunk is
+  // then loaded twice).
   if (nfull > 0) {
-    constexpr bool kEpilogue = G < 8;
+    constexpr bool kEpilogue = MF || G < 8;
     uint4 ka[U], va[U], kb[U], vb[U];
     issue(lookup(0), ka, va);
     Lookup next = lookup(1);
@@ -667,28 +852,28 @@ void decode_split_kernel(DecodeArgs a) {
       const Lookup after = lookup(i + 2);
       issue(next, kb, vb);  // chunk i+1
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the multiply
-      compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
+      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, ka, va);
       drain_loads<U, DRAIN>();
       next = lookup(i + 3);
       issue(after, ka, va);  // chunk i+2 (clamped)
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
+      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, kb, vb);
     }
     if (kEpilogue && i + 1 < nfull) {
       drain_loads<U, DRAIN>();
       issue(next, kb, vb);  // chunk i+1
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
-      compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, kb, vb);
+      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, ka, va);
+      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, kb, vb);
     } else if (i < nfull) {
-      compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, ka, va);
+      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, ka, va);
     }
   }
 #else
   for (int i = 0; i < nfull; ++i) {
     uint4 kr[U], vr[U];
     issue(lookup(i), kr, vr);
-    compute_chunk<L, D, G, U, false>(st, a.scale_log2, row, CHUNK, kr, vr);
+    compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, kr, vr);
   }
 #endif
   const int c = start + nfull * CHUNK;
@@ -703,7 +888,7 @@ void decode_split_kernel(DecodeArgs a) {
       kr[u] = load16(kc + off);
       vr[u] = load16(vc + off);
     }
-    compute_chunk<L, D, G, U, true>(st, a.scale_log2, row, cend - c, kr, vr);
+    compute_chunk<L, D, G, U, true>(st, lds, a.scale_log2, row, cend - c, kr, vr);
   }
   if (FUSED && end == n) {
     // the newest token: attend to it from registers and write it to its slot
@@ -712,7 +897,7 @@ void decode_split_kernel(DecodeArgs a) {
     const uint4 vt = *reinterpret_cast<const uint4*>(a.v_new + (int64_t)b * a.v_new_stride + g * D + sub * 8);
     const uint4 kr1[1] = {kt};
     const uint4 vr1[1] = {vt};
-    compute_chunk<L, D, G, 1, true>(st, a.scale_log2, row, 1, kr1, vr1);
+    compute_chunk<L, D, G, 1, true>(st, lds, a.scale_log2, row, 1, kr1, vr1);
     const int slot = a.slot_mapping[b];
     if (row == 0 && half == 0 && slot >= 0 && slot < (a.num_blocks << a.block_shift)) {
       const int64_t dst = (int64_t)slot * H_kv * D + g * D + sub * 8;
@@ -721,52 +906,82 @@ void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  // Merge the token-rows of lanes (each has its own running max); lanes
-  // SEG apart hold the same kv-head.
+  if constexpr (MF) {
+    // column sums across the 4 lane groups; the max is already common
+    const int lg = lane >> 4, li = lane & 15;
+    float lt = st.l;
+    lt += xor_lane(lt, 16);
+    lt += xor_lane(lt, 32);
+    if (li < G) {
+      if (parts.k == 1) {
+        const float inv = 1.f / lt;
+        uint16_t* dst = a.out + (head0 + li) * D + 4 * lg;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float M = st.m[h];
+        for (int mt = 0; mt < 8; ++mt) {
+          uint2 v;
+          v.x = pack_bf16x2(st.o[mt][0] * inv, st.o[mt][1] * inv);
+          v.y = pack_bf16x2(st.o[mt][2] * inv, st.o[mt][3] * inv);
+          *reinterpret_cast<uint2*>(dst + 16 * mt) = v;
+        }
+      } else {
+        const int64_t wi = (head0 + li) * a.max_parts + part;
+        float* dst = a.ws_o + wi * D + 4 * lg;
 #pragma unroll
-    for (int off = SEG; off < kWave; off <<= 1) M = fmaxf(M, xor_lane(M, off));
-    const float w = (st.m[h] == -INFINITY) ? 0.f : exp2f(st.m[h] - M);
-    float lh = st.l[h] * w;
-#pragma unroll
-    for (int off = SEG; off < kWave; off <<= 1) lh += xor_lane(lh, off);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float o = st.acc[h][e] * w;
-#pragma unroll
-      for (int off = SEG; off < kWave; off <<= 1) o += xor_lane(o, off);
-      st.acc[h][e] = o;
-    }
-    st.m[h] = M;
-    st.l[h] = lh;
-  }
-
-  if (parts.k == 1) {
-    if (row == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float inv = 1.f / st.l[h];
-        uint4 o;
-        o.x = pack_bf16x2(st.acc[h][0] * inv, st.acc[h][1] * inv);
-        o.y = pack_bf16x2(st.acc[h][2] * inv, st.acc[h][3] * inv);
-        o.z = pack_bf16x2(st.acc[h][4] * inv, st.acc[h][5] * inv);
-        o.w = pack_bf16x2(st.acc[h][6] * inv, st.acc[h][7] * inv);
-        *reinterpret_cast<uint4*>(a.out + (head0 + h) * D + sub * 8) = o;
+        for (int mt = 0; mt < 8; ++mt)
+          *reinterpret_cast<float4*>(dst + 16 * mt) =
+              make_float4(st.o[mt][0], st.o[mt][1], st.o[mt][2], st.o[mt][3]);
+        if (lg == 0) *reinterpret_cast<float2*>(a.ws_ml + wi * 2) = make_float2(st.m, lt);
       }
     }
+    return;
   } else {
-#pragma unroll
+    // Merge the token-rows of lanes (each has its own running max); lanes
+    // SEG apart hold the same kv-head.
+  #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const int64_t wi = (head0 + h) * a.max_parts + part;
-      if (row == 0) {
-        float4* dst = reinterpret_cast<float4*>(a.ws_o + wi * D + sub * 8);
-        dst[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
-        dst[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
+      float M = st.m[h];
+  #pragma unroll
+      for (int off = SEG; off < kWave; off <<= 1) M = fmaxf(M, xor_lane(M, off));
+      const float w = (st.m[h] == -INFINITY) ? 0.f : exp2f(st.m[h] - M);
+      float lh = st.l[h] * w;
+  #pragma unroll
+      for (int off = SEG; off < kWave; off <<= 1) lh += xor_lane(lh, off);
+  #pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float o = st.acc[h][e] * w;
+  #pragma unroll
+        for (int off = SEG; off < kWave; off <<= 1) o += xor_lane(o, off);
+        st.acc[h][e] = o;
       }
-      if (row == 0 && sub == 0)
-        *reinterpret_cast<float2*>(a.ws_ml + wi * 2) = make_float2(st.m[h], st.l[h]);
+      st.m[h] = M;
+      st.l[h] = lh;
+    }
+
+    if (parts.k == 1) {
+      if (row == 0) {
+  #pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float inv = 1.f / st.l[h];
+          uint4 o;
+          o.x = pack_bf16x2(st.acc[h][0] * inv, st.acc[h][1] * inv);
+          o.y = pack_bf16x2(st.acc[h][2] * inv, st.acc[h][3] * inv);
+          o.z = pack_bf16x2(st.acc[h][4] * inv, st.acc[h][5] * inv);
+          o.w = pack_bf16x2(st.acc[h][6] * inv, st.acc[h][7] * inv);
+          *reinterpret_cast<uint4*>(a.out + (head0 + h) * D + sub * 8) = o;
+        }
+      }
+    } else {
+  #pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const int64_t wi = (head0 + h) * a.max_parts + part;
+        if (row == 0) {
+          float4* dst = reinterpret_cast<float4*>(a.ws_o + wi * D + sub * 8);
+          dst[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
+          dst[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
+        }
+        if (row == 0 && sub == 0)
+          *reinterpret_cast<float2*>(a.ws_ml + wi * 2) = make_float2(st.m[h], st.l[h]);
+      }
     }
   }
 }
@@ -825,6 +1040,26 @@ SplitFn pick_split(int G) {
   return nullptr;
 }
 
+// The matrix-core variant (d = 128, one kv-head per wave).
+template <bool FUSED, bool SMALL, bool DRAIN>
+SplitFn pick_split_mf(int G) {
+  constexpr bool kD = DRAIN && !SMALL;
+  switch (G) {
+    case 1: return decode_split_kernel<128, 1, 1, FUSED, SMALL, kD, 1, true>;
+    case 2: return decode_split_kernel<128, 2, 1, FUSED, SMALL, kD, 1, true>;
+    case 4: return decode_split_kernel<128, 4, 1, FUSED, SMALL, kD, 1, true>;
+    case 8: return decode_split_kernel<128, 8, 1, FUSED, SMALL, kD, 1, true>;
+    case 16: return decode_split_kernel<128, 16, 1, FUSED, SMALL, kD, 1, true>;
+  }
+  return nullptr;
+}
+
+template <bool FUSED>
+SplitFn pick_split_mf(int G, bool small, bool drain) {
+  if (small) return pick_split_mf<FUSED, true, false>(G);
+  return drain ? pick_split_mf<FUSED, false, true>(G) : pick_split_mf<FUSED, false, false>(G);
+}
+
 template <int D, int KPW, bool FUSED>
 SplitFn pick_split(int G, bool small, bool drain) {
   if (small) return pick_split<D, KPW, FUSED, true, false>(G);
@@ -844,16 +1079,25 @@ SplitFn pick_split(int G, bool fused, bool small, bool drain) {
 // contiguous piece of each token row (on MI355X 512-byte pieces stream about
 // 7% faster than 256-byte ones), when the head count allows it; else one.
 // With 8 q-heads per kv-head the wave's arithmetic per byte is highest and
-// its chunks are shortest; there one kv-head per wave measures faster.
-// Waves per kv-head: a wave holds at most 8 q-heads, so 16 q-heads per
-// kv-head take two waves of one workgroup.
-int kv_split(const pa_desc* d) { return d->num_q_heads / d->num_kv_heads > 8 ? 2 : 1; }
+// its chunks are shortest; there one kv-head per wave measures faster (and
+// the matrix-core variant takes one kv-head per wave).
+// Waves per kv-head: a vector-path wave holds at most 8 q-heads, so 16
+// q-heads per kv-head take two waves of one workgroup at d = 64.
+#ifndef PA_DECODE_MF_MIN_G
+#define PA_DECODE_MF_MIN_G 8
+#endif
+// Group sizes from PA_DECODE_MF_MIN_G up run on the matrix cores at d = 128.
+bool use_mf(const pa_desc* d) {
+  return d->head_dim == 128 && d->num_q_heads / d->num_kv_heads >= PA_DECODE_MF_MIN_G;
+}
+int kv_split(const pa_desc* d) { return d->num_q_heads / d->num_kv_heads > 8 && !use_mf(d) ? 2 : 1; }
 
 // Work-item groups per sequence: kv-heads over kv-heads per wave.
 int item_groups(const pa_desc* d);
 
 int kv_heads_per_wave(int head_dim, int num_q_heads, int num_kv_heads) {
   if (num_q_heads / num_kv_heads >= 8) return 1;
+  if (head_dim == 128 && num_q_heads / num_kv_heads >= PA_DECODE_MF_MIN_G) return 1;
   const int want = PA_DECODE_SEGMENT / (2 * head_dim);
   return (want > 1 && num_kv_heads % want == 0) ? want : 1;
 }
@@ -998,13 +1242,16 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.order = plan.ordered ? (int32_t*)((char*)workspace + plan.partial_bytes) : nullptr;
 
   hipStream_t s = (hipStream_t)stream;
-  const int chunk = (kWave / (D / 8 * kpw)) * unroll_for(min(G, 8));  // tokens per chunk
+  const bool mf = use_mf(desc);
+  const int chunk = (kWave / (D / 8 * kpw)) * (mf ? 8 : unroll_for(min(G, 8)));  // tokens per chunk
   const bool small = desc->block_size < chunk;
   const bool fused = nt != nullptr;
   // the wave slots are full (2 per SIMD): one chunk of loads in flight per wave
   const bool drain = items >= kResidentItems;
   SplitFn split = nullptr;
-  if (D == 128) {
+  if (mf) {
+    split = fused ? pick_split_mf<true>(G, small, drain) : pick_split_mf<false>(G, small, drain);
+  } else if (D == 128) {
     split = kpw == 2 ? pick_split<128, 2>(G, fused, small, drain)
                      : pick_split<128, 1>(G, fused, small, drain);
   } else {

@@ -147,9 +147,10 @@ def test_padding_rows_and_skipped_slots():
 
 
 @pytest.mark.parametrize("partition_blocks", [1, 2, 3, 64])
-def test_partition_size_invariance(partition_blocks):
+@pytest.mark.parametrize("h_q,h_kv", [(32, 8), (64, 4)])
+def test_partition_size_invariance(partition_blocks, h_q, h_kv):
     lens = [1, 256, 700, 3000, 5000, 8192]
-    case = W.decode_case(32, 8, 128, lens, seed=74)
+    case = W.decode_case(h_q, h_kv, 128, lens, seed=74)
     out, caches, slots, before = run_decode_step(case, partition_blocks=partition_blocks)
     kc_ref, vc_ref = check_store(case, caches, slots, before)
     check_decode(case, out, kc_ref, vc_ref)
@@ -188,8 +189,8 @@ def test_prefill_store_bit_exact():
     assert np.array_equal(host_bits(kc), kref) and np.array_equal(host_bits(vc), vref)
 
 
-@pytest.mark.parametrize("batch,h_q,h_kv,d", [(1536, 32, 8, 128), (4096, 8, 2, 64),
-                                              (4097, 8, 2, 64)])
+@pytest.mark.parametrize("batch,h_q,h_kv,d", [(1536, 32, 8, 128), (1536, 64, 8, 128),
+                                              (4096, 8, 2, 64), (4097, 8, 2, 64)])
 def test_large_batch_of_short_sequences(batch, h_q, h_kv, d):
     """Large batches of short sequences: up to 4,096 sequences the items are
     ranked by the order kernel (sequence ids fill its 12 bits at 4,096), one
@@ -207,3 +208,24 @@ def test_large_batch_of_short_sequences(batch, h_q, h_kv, d):
                   {batch - 2, 4095 if batch > 4095 else 0})
     check_decode(case, out, kc_ref, vc_ref, rows=rows)
     assert np.all(out[pad] == 0)
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(32, 8), (64, 8), (64, 4)])
+def test_running_max_moves_many_times(h_q, h_kv):
+    """Keys grow along each sequence (factor 0.2 .. 6.2), so every q-head's
+    running max rises chunk after chunk, by far more than 2^8 in log2 units
+    over a long sequence, and the newest token is among the largest: every
+    rescaling step (exact on the vector path, deferred until the max has
+    grown by 2^8 on the matrix-core path) runs."""
+    lens = [40, 700, 3000]
+    case = W.decode_case(h_q, h_kv, 128, lens, seed=79)
+    kf = oracle.bf16_bits_to_f64(case.k_cache)
+    bsz = case.block_size
+    for b, n in enumerate(lens):
+        for p in range(n - 1):  # the newest token (n - 1) comes from k_new
+            kf[case.block_tables[b, p // bsz], p % bsz] *= 0.2 + 6.0 * p / n
+    case.k_cache = W.round_to_bf16_bits(kf)
+    case.k_new = W.round_to_bf16_bits(oracle.bf16_bits_to_f64(case.k_new) * 6.2)
+    out, caches, slots, before = run_decode_step(case, poison=True)
+    kc_ref, vc_ref = check_store(case, caches, slots, before)
+    check_decode(case, out, kc_ref, vc_ref)
