@@ -75,17 +75,17 @@ def src_hash(path: str) -> str:
 
 
 def traffic_from_profile(pmc_file: str, kernel_src: str, mode: str | None,
-                         block_size: int = 256):
+                         block_size: int = 256, config: str | None = None):
     """HBM bytes per launch of a call from a committed rocprofv3 counter
-    summary, or None if it is missing, was taken for another step mode or
-    block size, or on a different kernel source."""
+    summary, or None if it is missing, was taken for another workload, step
+    mode or block size, or on a different kernel source."""
     try:
         with open(pmc_file) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     if (rec.get("source_sha256_16") != src_hash(kernel_src) or rec.get("step_mode") != mode
-            or rec.get("block_size") != block_size):
+            or rec.get("block_size") != block_size or rec.get("config") != config):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -432,7 +432,7 @@ def main() -> int:
         dom, dom_bytes = "pa_decode", db
         dom_desc = "pa_decode (order + split-K + merge)"
     dom_gbs = dom_bytes / (ms_call[dom] * 1e-3) / 1e9
-    traffic = traffic_from_profile(PMC_FILE, DECODE_SRC, args.mode, args.block_size)
+    traffic = traffic_from_profile(PMC_FILE, DECODE_SRC, args.mode, args.block_size, args.config)
 
     rec = {
         "metric": "paged decode: KV GB/s (% HBM peak) + tokens/s at Qwen3-8B shape, batch 256",
