@@ -490,7 +490,7 @@ template <bool TAIL>
 __device__ __forceinline__ void compute_chunk_mf(MfState& st, char* lds, float scale_log2,
                                                  int nvalid, const uint4 (&kr)[8],
                                                  const uint4 (&vr)[8]) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
   const int g = lane >> 4, i = lane & 15;
   char* vt = lds + kMfKBytes;
 #pragma unroll
@@ -709,11 +709,13 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
 // VS waves per workgroup share a kv-head, each with G of its q-heads (VS = 2
 // at 16 q-heads per kv-head: a wave holds at most 8); they read the same
 // K/V rows on the same CU, so the second read is served by its caches.
-// MF: the matrix-core variant (d = 128, KPW = 1, VS = 1, G <= 16).
+// MF: the matrix-core variant (d = 128, KPW = 1, G <= 16); with VS > 1 its
+// waves take VS adjacent kv-heads, one each.
 template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1, bool MF = false>
 __global__ __launch_bounds__(kWave * VS) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
 void decode_split_kernel(DecodeArgs a) {
-  static_assert(!MF || (D == 128 && KPW == 1 && VS == 1 && G <= 16), "matrix-core geometry");
+  static_assert(!MF || (D == 128 && KPW == 1 && G <= 16 && VS <= 4), "matrix-core geometry");
+  constexpr bool kPair = MF && VS > 1;  // one kv-head per wave, VS per workgroup
   constexpr int U = MF ? 8 : unroll_for(G);
   using S = typename std::conditional<MF, MfState, SplitState<D, G>>::type;
   using L = Lanes<D, KPW>;
@@ -724,8 +726,9 @@ void decode_split_kernel(DecodeArgs a) {
   static_assert(kMinBlockSize % TPI == 0, "a load group never straddles a block");
 
   const int H_kv = a.num_kv_heads;
-  const int H_q = H_kv * G * VS;
-  const int n_groups = H_kv / KPW;  // kv-head groups (the host checks divisibility)
+  const int H_q = H_kv * G * (kPair ? 1 : VS);
+  // kv-head groups (the host checks divisibility)
+  const int n_groups = H_kv / (kPair ? VS : KPW);
   const int gw = blockIdx.x % n_groups;  // the kv-head groups of one item are adjacent
   int b, part;
   if (a.order) {
@@ -741,14 +744,16 @@ void decode_split_kernel(DecodeArgs a) {
     part = a.max_parts - 1 - idx / a.num_seqs;
   }
   const int lane = threadIdx.x % kWave;
-  const int half = VS == 1 ? 0 : threadIdx.x / kWave;  // which G q-heads of the kv-head
+  // which G q-heads of the kv-head (or, kPair, which kv-head of the VS)
+  const int half = VS == 1 ? 0 : threadIdx.x / kWave;
   const int sub = lane % LPT;                 // which 8 elements of the head vector
-  const int g = gw * KPW + (lane / LPT) % KPW;  // this lane's kv-head
+  const int g = kPair ? gw * VS + half : gw * KPW + (lane / LPT) % KPW;  // this lane's kv-head
   const int row = lane / SEG;                 // which token of a load instruction
 
   const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
   const Parts parts = split_parts(n, a.part_tokens, a.max_parts);
-  const int64_t head0 = (int64_t)b * H_q + (int64_t)g * G * VS + half * G;  // first q-head
+  const int64_t head0 = kPair ? (int64_t)b * H_q + (int64_t)g * G
+                              : (int64_t)b * H_q + (int64_t)g * G * VS + half * G;  // first q-head
 
   if (n == 0) {  // padding row: defined as zeros, nothing read
     if (part == 0 && row == 0) {
@@ -766,8 +771,8 @@ void decode_split_kernel(DecodeArgs a) {
   S st;
   char* lds = nullptr;
   if constexpr (MF) {
-    __shared__ __attribute__((aligned(16))) char mf_lds[kMfBytes];
-    lds = mf_lds;
+    __shared__ __attribute__((aligned(16))) char mf_lds[VS * kMfBytes];
+    lds = mf_lds + half * kMfBytes;
     // lane (g, i): q-head i (zeros past G), elements 32j + 8g .. +8
     const int qg = lane >> 4, qi = lane & 15;
 #pragma unroll
@@ -899,7 +904,7 @@ void decode_split_kernel(DecodeArgs a) {
     const uint4 vr1[1] = {vt};
     compute_chunk<L, D, G, 1, true>(st, lds, a.scale_log2, row, 1, kr1, vr1);
     const int slot = a.slot_mapping[b];
-    if (row == 0 && half == 0 && slot >= 0 && slot < (a.num_blocks << a.block_shift)) {
+    if (row == 0 && (kPair || half == 0) && slot >= 0 && slot < (a.num_blocks << a.block_shift)) {
       const int64_t dst = (int64_t)slot * H_kv * D + g * D + sub * 8;
       *reinterpret_cast<uint4*>(a.k_cache_w + dst) = kt;
       *reinterpret_cast<uint4*>(a.v_cache_w + dst) = vt;
@@ -1040,24 +1045,36 @@ SplitFn pick_split(int G) {
   return nullptr;
 }
 
-// The matrix-core variant (d = 128, one kv-head per wave).
-template <bool FUSED, bool SMALL, bool DRAIN>
+// The matrix-core variant (d = 128, one kv-head per wave, VS waves per
+// workgroup).
+template <bool FUSED, bool SMALL, bool DRAIN, int VS>
 SplitFn pick_split_mf(int G) {
   constexpr bool kD = DRAIN && !SMALL;
   switch (G) {
-    case 1: return decode_split_kernel<128, 1, 1, FUSED, SMALL, kD, 1, true>;
-    case 2: return decode_split_kernel<128, 2, 1, FUSED, SMALL, kD, 1, true>;
-    case 4: return decode_split_kernel<128, 4, 1, FUSED, SMALL, kD, 1, true>;
-    case 8: return decode_split_kernel<128, 8, 1, FUSED, SMALL, kD, 1, true>;
-    case 16: return decode_split_kernel<128, 16, 1, FUSED, SMALL, kD, 1, true>;
+    case 1: return decode_split_kernel<128, 1, 1, FUSED, SMALL, kD, VS, true>;
+    case 2: return decode_split_kernel<128, 2, 1, FUSED, SMALL, kD, VS, true>;
+    case 4: return decode_split_kernel<128, 4, 1, FUSED, SMALL, kD, VS, true>;
+    case 8: return decode_split_kernel<128, 8, 1, FUSED, SMALL, kD, VS, true>;
+    case 16: return decode_split_kernel<128, 16, 1, FUSED, SMALL, kD, VS, true>;
   }
   return nullptr;
 }
 
-template <bool FUSED>
+template <bool FUSED, int VS>
 SplitFn pick_split_mf(int G, bool small, bool drain) {
-  if (small) return pick_split_mf<FUSED, true, false>(G);
-  return drain ? pick_split_mf<FUSED, false, true>(G) : pick_split_mf<FUSED, false, false>(G);
+  if (small) return pick_split_mf<FUSED, true, false, VS>(G);
+  return drain ? pick_split_mf<FUSED, false, true, VS>(G)
+               : pick_split_mf<FUSED, false, false, VS>(G);
+}
+
+template <bool FUSED>
+SplitFn pick_split_mf(int G, bool small, bool drain, int waves) {
+  switch (waves) {
+    case 1: return pick_split_mf<FUSED, 1>(G, small, drain);
+    case 2: return pick_split_mf<FUSED, 2>(G, small, drain);
+    case 4: return pick_split_mf<FUSED, 4>(G, small, drain);
+  }
+  return nullptr;
 }
 
 template <int D, int KPW, bool FUSED>
@@ -1090,7 +1107,21 @@ SplitFn pick_split(int G, bool fused, bool small, bool drain) {
 bool use_mf(const pa_desc* d) {
   return d->head_dim == 128 && d->num_q_heads / d->num_kv_heads >= PA_DECODE_MF_MIN_G;
 }
-int kv_split(const pa_desc* d) { return d->num_q_heads / d->num_kv_heads > 8 && !use_mf(d) ? 2 : 1; }
+#ifndef PA_DECODE_MF_GROUP
+#define PA_DECODE_MF_GROUP 2
+#endif
+// Matrix-core items: PA_DECODE_MF_GROUP adjacent kv-heads (fewer when the
+// head count does not divide), one wave each, in one workgroup.
+int mf_waves(const pa_desc* d) {
+  if (!use_mf(d)) return 0;
+  int w = PA_DECODE_MF_GROUP;
+  while (w > 1 && d->num_kv_heads % w) w >>= 1;
+  return w;
+}
+int kv_split(const pa_desc* d) {
+  if (use_mf(d)) return mf_waves(d);
+  return d->num_q_heads / d->num_kv_heads > 8 ? 2 : 1;
+}
 
 // Work-item groups per sequence: kv-heads over kv-heads per wave.
 int item_groups(const pa_desc* d);
@@ -1103,6 +1134,7 @@ int kv_heads_per_wave(int head_dim, int num_q_heads, int num_kv_heads) {
 }
 
 int item_groups(const pa_desc* d) {
+  if (use_mf(d)) return d->num_kv_heads / mf_waves(d);
   return d->num_kv_heads / kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
 }
 
@@ -1115,8 +1147,9 @@ constexpr int kPartUnit = 256;
 constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kResidentItems = kComputeUnits * 8;
 
-// Longest partition (16 (multi-head waves only), 8, 4, 2 or 1 units of 256
-// tokens) whose item count still fills half the resident slots, estimating
+// Longest partition (16 (multi-head waves and the matrix-core variant only),
+// 8, 4, 2 or 1 units of 256 tokens) whose wave count still fills half the
+// resident slots, estimating
 // the mean context as max_context_len / 2. Long partitions amortise each
 // item's set-up and keep its loads streaming (fewer concurrent streams also
 // read HBM more efficiently); short ones keep small batches spread over the
@@ -1124,10 +1157,16 @@ constexpr int64_t kResidentItems = kComputeUnits * 8;
 int default_partition_blocks(const pa_desc* d, int32_t num_seqs, int32_t max_ctx) {
   const int64_t mean_ctx = max(1, max_ctx / 2);
   const int kpw = kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
-  const int groups = item_groups(d);
-  for (int p = kpw > 1 ? 16 : 8; p > 1; p >>= 1) {
+  // waves per sequence and partition (a matrix-core item is one per kv-head);
+  // matrix-core items of two waves keep long partitions down to a quarter
+  // of the slots (64 q / 8 kv heads at batch 64: 186 us with 4,096 tokens,
+  // 195 us with 2,048)
+  const bool mf = use_mf(d);
+  const int groups = mf ? d->num_kv_heads : item_groups(d);
+  const int64_t fill = mf && mf_waves(d) > 1 ? kResidentItems / 4 : kResidentItems / 2;
+  for (int p = (kpw > 1 || mf) ? 16 : 8; p > 1; p >>= 1) {
     const int64_t per_seq = (mean_ctx + (int64_t)p * kPartUnit - 1) / ((int64_t)p * kPartUnit);
-    if ((int64_t)num_seqs * groups * per_seq >= kResidentItems / 2) return p;
+    if ((int64_t)num_seqs * groups * per_seq >= fill) return p;
   }
   return 1;
 }
@@ -1250,7 +1289,9 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   const bool drain = items >= kResidentItems;
   SplitFn split = nullptr;
   if (mf) {
-    split = fused ? pick_split_mf<true>(G, small, drain) : pick_split_mf<false>(G, small, drain);
+    const int waves = mf_waves(desc);
+    split = fused ? pick_split_mf<true>(G, small, drain, waves)
+                  : pick_split_mf<false>(G, small, drain, waves);
   } else if (D == 128) {
     split = kpw == 2 ? pick_split<128, 2>(G, fused, small, drain)
                      : pick_split<128, 1>(G, fused, small, drain);
