@@ -275,7 +275,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="qwen3-8b", choices=["qwen3-8b", "qwen3-0.6b", "long"])
+    ap.add_argument("--config", default="qwen3-8b",
+                    choices=["qwen3-8b", "qwen3-0.6b", "long", "gqa8", "gqa16"])
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--prefill", action="store_true", help="also time the prefill workload")
@@ -454,15 +455,16 @@ def main() -> int:
                    "block_size": case.block_size, "pool_replicas": len(pools),
                    "step_mode": args.mode + (" + hip graph" if args.graph else "")},
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
-        "tokens_per_s": {"per_layer": round(case.batch / (ms_step * 1e-3), 1),
-                         "model_36_layers": round(case.batch / (LAYERS_QWEN3_8B * ms_step * 1e-3),
-                                                  1)},
+        "tokens_per_s": {"per_layer": round(case.batch / (ms_step * 1e-3), 1)},
         "ms_per_call": {k: round(v, 5) for k, v in ms_call.items()},
         "algorithmic_bytes": {"decode": db, "store": sb},
         "roofline": {"bound": "hbm", "kernel": dom_desc,
                      "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if args.config == "qwen3-8b":
+        rec["tokens_per_s"]["model_36_layers"] = round(
+            case.batch / (LAYERS_QWEN3_8B * ms_step * 1e-3), 1)
     if args.prefill:
         rec["prefill"] = run_prefill(args, torch, B, W, dev)
     if args.mixed:

@@ -259,7 +259,7 @@ def mixed_case(num_q_heads: int, num_kv_heads: int, head_dim: int, decode_lens, 
 # ------------------------------------------------------------ named workloads
 
 SEEDS = {"tiny": 1001, "qwen3-0.6b": 1002, "qwen3-8b": 1003, "long": 1004, "prefill": 1005,
-         "mixed": 1006}
+         "mixed": 1006, "gqa8": 1007, "gqa16": 1008}
 
 DESCRIPTIONS = {
     "tiny": "decode, 4 q / 2 kv heads, d 64, B 256, pool 16, ctx {1,17,256,300}",
@@ -271,6 +271,10 @@ DESCRIPTIONS = {
     "mixed": "mixed varlen step, 32 q / 8 kv heads, d 128, B 256: 224 decode rows "
              "(ctx U[512,8192]) + 4 chunked-prefill rows of 512 tokens starting mid-block "
              "(cached U[100,4000])",
+    # larger GQA groups than the pages' shapes, same batch and lengths as
+    # qwen3-8b: 8 and 16 q-heads per kv-head
+    "gqa8": "decode, 64 q / 8 kv heads, d 128, B 256, 256 seqs, ctx U[512,8192]",
+    "gqa16": "decode, 64 q / 4 kv heads, d 128, B 256, 256 seqs, ctx U[512,8192]",
 }
 
 
@@ -292,6 +296,9 @@ def make_case(name: str, seed: int | None = None, threads: int | None = None,
         return decode_case(32, 8, 128, ctx, seed + 1, **kw)
     if name == "long":
         return decode_case(32, 8, 128, [16384] * 32, seed + 1, **kw)
+    if name in ("gqa8", "gqa16"):  # the qwen3-8b lengths, own contents
+        ctx = np.random.default_rng(SEEDS["qwen3-8b"]).integers(512, 8192 + 1, size=256)
+        return decode_case(64, 8 if name == "gqa8" else 4, 128, ctx, seed + 1, **kw)
     if name == "prefill":
         suffix = np.random.default_rng(seed).integers(100, 2000 + 1, size=16)
         return prefill_case(32, 8, 128, 1024, suffix, seed + 1, **kw)

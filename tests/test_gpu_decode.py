@@ -98,7 +98,7 @@ def _sample_rows(ctx, k, seed):
     return sorted(pick)
 
 
-@pytest.mark.parametrize("name", ["qwen3-8b", "long"])
+@pytest.mark.parametrize("name", ["qwen3-8b", "long", "gqa8", "gqa16"])
 def test_store_and_decode_full_size_sampled(name):
     """Full-size workloads in the benchmark's launch configuration; the store
     is compared in full, decode on sampled sequences (longest and shortest
@@ -106,7 +106,7 @@ def test_store_and_decode_full_size_sampled(name):
     case = W.make_case(name)
     out, caches, slots, before = run_decode_step(case)
     kc_ref, vc_ref = check_store(case, caches, slots, before)
-    rows = _sample_rows(case.context_lens, 6 if name == "qwen3-8b" else 3, 5)
+    rows = _sample_rows(case.context_lens, 3 if name == "long" else 6, 5)
     check_decode(case, out, kc_ref, vc_ref, rows=rows)
 
 
