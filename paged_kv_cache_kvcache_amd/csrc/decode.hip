@@ -81,6 +81,7 @@ struct DecodeArgs {
   int32_t block_size;   // tokens per physical block (power of two)
   int32_t block_shift;  // log2(block_size)
   int32_t* order;  // dispatch order (decode_order_kernel), or null: plain order
+  int32_t group;   // q-heads per kv-head
   float scale_log2;
 };
 
@@ -709,15 +710,18 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
 // VS waves per workgroup share a kv-head, each with G of its q-heads (VS = 2
 // at 16 q-heads per kv-head: a wave holds at most 8); they read the same
 // K/V rows on the same CU, so the second read is served by its caches.
-// MF: the matrix-core variant (d = 128, KPW = 1, G <= 16); with VS > 1 its
-// waves take VS adjacent kv-heads, one each.
+// MF: the matrix-core variant (d = 128, KPW = 1, G <= 16; G = 0 takes the
+// group size from the arguments); with VS > 1 its waves take VS adjacent
+// kv-heads, one each.
 template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1, bool MF = false>
 __global__ __launch_bounds__(kWave * VS) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
 void decode_split_kernel(DecodeArgs a) {
   static_assert(!MF || (D == 128 && KPW == 1 && G <= 16 && VS <= 4), "matrix-core geometry");
+  static_assert(MF || G > 0, "the vector path is built per group size");
+  const int Gn = G ? G : a.group;  // q-heads per kv-head
   constexpr bool kPair = MF && VS > 1;  // one kv-head per wave, VS per workgroup
   constexpr int U = MF ? 8 : unroll_for(G);
-  using S = typename std::conditional<MF, MfState, SplitState<D, G>>::type;
+  using S = typename std::conditional<MF, MfState, SplitState<D, (G ? G : 1)>>::type;
   using L = Lanes<D, KPW>;
   constexpr int LPT = L::LPT;
   constexpr int SEG = L::SEG;
@@ -726,7 +730,7 @@ void decode_split_kernel(DecodeArgs a) {
   static_assert(kMinBlockSize % TPI == 0, "a load group never straddles a block");
 
   const int H_kv = a.num_kv_heads;
-  const int H_q = H_kv * G * (kPair ? 1 : VS);
+  const int H_q = H_kv * Gn * (kPair ? 1 : VS);
   // kv-head groups (the host checks divisibility)
   const int n_groups = H_kv / (kPair ? VS : KPW);
   const int gw = blockIdx.x % n_groups;  // the kv-head groups of one item are adjacent
@@ -752,13 +756,13 @@ void decode_split_kernel(DecodeArgs a) {
 
   const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
   const Parts parts = split_parts(n, a.part_tokens, a.max_parts);
-  const int64_t head0 = kPair ? (int64_t)b * H_q + (int64_t)g * G
-                              : (int64_t)b * H_q + (int64_t)g * G * VS + half * G;  // first q-head
+  const int64_t head0 = kPair ? (int64_t)b * H_q + (int64_t)g * Gn
+                              : (int64_t)b * H_q + (int64_t)g * Gn * VS + half * Gn;  // first q-head
 
   if (n == 0) {  // padding row: defined as zeros, nothing read
     if (part == 0 && row == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int h = 0; h < Gn; ++h)
         *reinterpret_cast<uint4*>(a.out + (head0 + h) * D + sub * 8) = make_uint4(0, 0, 0, 0);
     }
     return;
@@ -778,7 +782,7 @@ void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint4 t = make_uint4(0, 0, 0, 0);
-      if (qi < G) t = *reinterpret_cast<const uint4*>(a.q + (head0 + qi) * D + 32 * j + 8 * qg);
+      if (qi < Gn) t = *reinterpret_cast<const uint4*>(a.q + (head0 + qi) * D + 32 * j + 8 * qg);
       st.qf[j] = __builtin_bit_cast(bf16x8, t);
     }
     st.m = -INFINITY;
@@ -917,7 +921,7 @@ void decode_split_kernel(DecodeArgs a) {
     float lt = st.l;
     lt += xor_lane(lt, 16);
     lt += xor_lane(lt, 32);
-    if (li < G) {
+    if (li < Gn) {
       if (parts.k == 1) {
         const float inv = 1.f / lt;
         uint16_t* dst = a.out + (head0 + li) * D + 4 * lg;
@@ -1057,7 +1061,7 @@ SplitFn pick_split_mf(int G) {
     case 8: return decode_split_kernel<128, 8, 1, FUSED, SMALL, kD, VS, true>;
     case 16: return decode_split_kernel<128, 16, 1, FUSED, SMALL, kD, VS, true>;
   }
-  return nullptr;
+  return G >= 1 && G <= 16 ? decode_split_kernel<128, 0, 1, FUSED, SMALL, kD, VS, true> : nullptr;
 }
 
 template <bool FUSED, int VS>
@@ -1103,10 +1107,12 @@ SplitFn pick_split(int G, bool fused, bool small, bool drain) {
 #ifndef PA_DECODE_MF_MIN_G
 #define PA_DECODE_MF_MIN_G 8
 #endif
-// Group sizes from PA_DECODE_MF_MIN_G up run on the matrix cores at d = 128.
-bool use_mf(const pa_desc* d) {
-  return d->head_dim == 128 && d->num_q_heads / d->num_kv_heads >= PA_DECODE_MF_MIN_G;
+// Group sizes from PA_DECODE_MF_MIN_G up, and those that are not powers of
+// two, run on the matrix cores at d = 128.
+bool mf_group(int head_dim, int G) {
+  return head_dim == 128 && (G >= PA_DECODE_MF_MIN_G || (G & (G - 1)) != 0);
 }
+bool use_mf(const pa_desc* d) { return mf_group(d->head_dim, d->num_q_heads / d->num_kv_heads); }
 #ifndef PA_DECODE_MF_GROUP
 #define PA_DECODE_MF_GROUP 2
 #endif
@@ -1128,7 +1134,7 @@ int item_groups(const pa_desc* d);
 
 int kv_heads_per_wave(int head_dim, int num_q_heads, int num_kv_heads) {
   if (num_q_heads / num_kv_heads >= 8) return 1;
-  if (head_dim == 128 && num_q_heads / num_kv_heads >= PA_DECODE_MF_MIN_G) return 1;
+  if (mf_group(head_dim, num_q_heads / num_kv_heads)) return 1;
   const int want = PA_DECODE_SEGMENT / (2 * head_dim);
   return (want > 1 && num_kv_heads % want == 0) ? want : 1;
 }
@@ -1279,6 +1285,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.block_shift = log2_int(desc->block_size);
   a.scale_log2 = scale * kLog2e;
   a.order = plan.ordered ? (int32_t*)((char*)workspace + plan.partial_bytes) : nullptr;
+  a.group = G;
 
   hipStream_t s = (hipStream_t)stream;
   const bool mf = use_mf(desc);

@@ -55,7 +55,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaves = PA_PREFILL_WAVES;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr int kNT = PA_PREFILL_NT;        // 16-column tiles per wave
-constexpr int kCols = 16 * kNT * kWaves;  // (position, q-head) columns per workgroup
+constexpr int kTiles = kNT * kWaves;      // 16-column tiles per workgroup
+constexpr int kCols = 16 * kTiles;        // (position, q-head) columns per workgroup
 // Lazy rescaling: a column's reference max moves only when a score exceeds
 // it by more than 2^kLazyLog2 (weights stay <= 256, well inside bf16/fp32).
 constexpr float kLazyLog2 = 8.f;
@@ -76,8 +77,13 @@ struct PrefillArgs {
   int32_t max_rblocks;  // position blocks of the longest sequence
   int32_t block_size;   // tokens per physical block (power of two)
   int32_t block_shift;  // log2(block_size)
+  int32_t group;        // q-heads per kv-head
   float scale_log2;
 };
+
+// Query positions per workgroup: its tiles cover floor(kTiles / G) blocks of
+// 16 positions for all G q-heads (every tile when G divides kTiles).
+__host__ __device__ constexpr int positions_per_workgroup(int G) { return 16 * (kTiles / G); }
 
 template <int D>
 struct Geo {
@@ -197,10 +203,13 @@ __device__ __forceinline__ void store_stage(char* lds, const u32x4 (&kreg)[Geo<D
   }
 }
 
-template <int D, int G, bool SMALL>
+// G_ = 0: the group size is taken from the arguments (any G up to kTiles).
+template <int D, int G_, bool SMALL>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   using GG = Geo<D>;
-  constexpr int QB = kCols / G;              // query positions per workgroup
+  const int G = G_ ? G_ : a.group;
+  const int QB = positions_per_workgroup(G);  // query positions per workgroup
+  const int used = (kTiles / G) * G;          // tiles with columns of their own
   constexpr int KSTEPS = D / 32;             // MFMA k-steps over head_dim
   constexpr int MT = D / 16;                 // 16-row tiles of O^T over head_dim
   __shared__ __attribute__((aligned(16))) char lds[2 * GG::STAGE];
@@ -243,12 +252,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int grp = lane / 16;
 
   int head[kNT], pbase[kNT];
+  bool own[kNT];  // a spare tile (when G does not divide kTiles) repeats a used one, unwritten
   int wmax = -1;  // last position any column of this wave holds
 #pragma unroll
   for (int j = 0; j < kNT; ++j) {
     const int T = wave * kNT + j;
-    head[j] = g * G + T % G;
-    pbase[j] = p0 + (T / G) * 16;
+    own[j] = T < used;
+    const int Tu = own[j] ? T : T - used;
+    head[j] = g * G + Tu % G;
+    pbase[j] = p0 + (Tu / G) * 16;
     wmax = max(wmax, pbase[j] + 15);
   }
   wmax = min(wmax, p_end - 1);
@@ -397,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
     lt += xor_lane(lt, 16);
     lt += xor_lane(lt, 32);
     const int pos = pbase[j] + col;
-    if (pos < 0 || pos >= p_end) continue;
+    if (!own[j] || pos < 0 || pos >= p_end) continue;
     const float inv = 1.f / lt;
     uint16_t* dst = a.out + ((int64_t)(q0 + pos) * H_q + head[j]) * D + grp * 4;
 #pragma unroll
@@ -421,6 +433,8 @@ PrefillFn pick(int G) {
     case 8: return prefill_kernel<D, 8, SMALL>;
     case 16: return prefill_kernel<D, 16, SMALL>;
   }
+  // other group sizes (head_dim 128 only)
+  if constexpr (D == 128) return G >= 1 && G <= kTiles ? prefill_kernel<D, 0, SMALL> : nullptr;
   return nullptr;
 }
 
@@ -463,7 +477,7 @@ int launch_prefill(const char* who, const void* q, const void* k_cache, const vo
   }
   const int G = desc->num_q_heads / desc->num_kv_heads;
   const int D = desc->head_dim;
-  const int QB = kCols / G;
+  const int QB = positions_per_workgroup(G);
   const int64_t rblocks = (max_seqlen_q + QB - 1) / QB;
   const int64_t blocks = (int64_t)num_seqs * desc->num_kv_heads * rblocks;
   if (blocks > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "%s: grid too large", who);
@@ -483,6 +497,7 @@ int launch_prefill(const char* who, const void* q, const void* k_cache, const vo
   a.max_rblocks = (int32_t)rblocks;
   a.block_size = desc->block_size;
   a.block_shift = log2_int(desc->block_size);
+  a.group = G;
   a.scale_log2 = scale * kLog2e;
   const bool small = desc->block_size < kKT;
   PrefillFn fn = D == 128 ? (small ? pick<128, true>(G) : pick<128, false>(G))
