@@ -475,9 +475,12 @@ constexpr int kMfKBytes = 2 * 16 * 256;         // two 16-token K tiles, 256-byt
 constexpr int kMfVRow = 80;                      // V^T row: 32 keys x 2 B, padded
 constexpr int kMfBytes = kMfKBytes + 128 * kMfVRow;  // LDS per wave
 // A column's reference max moves only when a score exceeds it by more than
-// 2^kMfLazy (weights stay <= 256, exact in the fp32 sums).
+// kMfLazy in log2 units, so a weight stays below 2^8: far inside the bf16 and
+// fp32 ranges, and most chunks skip the rescale.
 constexpr float kMfLazy = 8.f;
 
+// acc + lo + hi of a packed bf16 pair, summed in fp32 (v_dot2_f32_bf16 with
+// the pair (1, 1)).
 __device__ __forceinline__ float sum_pair_bf16(uint32_t pair, float acc) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),

@@ -109,7 +109,7 @@ __device__ __forceinline__ int key_slot(int k) {
   return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
 }
 
-// acc + lo + hi of a packed bf16 pair, exactly in fp32 (v_dot2_f32_bf16 with
+// acc + lo + hi of a packed bf16 pair, summed in fp32 (v_dot2_f32_bf16 with
 // the pair (1.0, 1.0)).
 __device__ __forceinline__ float sum_pair_bf16(uint32_t pair, float acc) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;

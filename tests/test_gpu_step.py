@@ -55,9 +55,10 @@ def test_fused_step_full_oracle(name):
     check_step(case, host_f64(out), (kc, vc), (kc0, vc0), slots)
 
 
-def test_fused_step_full_size_and_matches_unfused():
-    case = W.make_case("qwen3-8b")
-    print("fused step: qwen3-8b", flush=True)
+@pytest.mark.parametrize("name", ["qwen3-8b", "gqa8"])
+def test_fused_step_full_size_and_matches_unfused(name):
+    case = W.make_case(name)
+    print("fused step: %s" % name, flush=True)
     slots = step_slots(case)
     kc, vc = dev_bf16(case.k_cache), dev_bf16(case.v_cache)
     q, k_new, v_new = dev_bf16(case.q), dev_bf16(case.k_new), dev_bf16(case.v_new)
@@ -99,14 +100,16 @@ def test_fused_step_padding_rows_and_strided_new_tokens():
     assert np.all(o[[0, 5]] == 0)
 
 
-def test_graph_replay_of_the_step_with_new_inputs():
+@pytest.mark.parametrize("h_q", [32, 64])
+def test_graph_replay_of_the_step_with_new_inputs(h_q):
     """The per-layer decode step captured once in a graph (static input
     buffers, padding rows with slot -1 / length 0, as a graph bucket would
     have), then replayed three times with new q, new tokens and longer
     contexts copied into the static buffers, with eager work between the
-    replays. Every replay must equal the oracle and the eager step."""
+    replays. Every replay must equal the oracle and the eager step. 64
+    q-heads per 8 kv-heads runs the matrix-core kernel (LDS staging)."""
     rng = np.random.default_rng(122)
-    h_q, h_kv, d, bsz = 32, 8, 128, 8
+    h_kv, d, bsz = 8, 128, 8
     base = [300, 1, 4000, 256, 700]  # 5 live rows, 3 padding rows
     max_blocks = 20
     nb = 128
