@@ -32,8 +32,7 @@
  *   - Supported shapes: head_dim 64 or 128; block_size a power of two in
  *     [16, 1024] (256 is the pages' size and the tuned one); num_q_heads a
  *     multiple of num_kv_heads with group size G = num_q_heads / num_kv_heads
- *     in 1 .. 16 at head_dim 128 and in {1, 2, 4, 8, 16} at head_dim 64.
- *     Others return PA_ERR_UNSUPPORTED.
+ *     in 1 .. 16. Others return PA_ERR_UNSUPPORTED.
  */
 #ifndef PA_H
 #define PA_H

@@ -45,9 +45,7 @@ int check_desc(const pa_desc* d) {
     return fail(PA_ERR_UNSUPPORTED, "block_size %d not built (powers of two, 16..1024)",
                 d->block_size);
   const int g = d->num_q_heads / d->num_kv_heads;
-  if (d->head_dim == 128 ? g > 16 : (g != 1 && g != 2 && g != 4 && g != 8 && g != 16))
-    return fail(PA_ERR_UNSUPPORTED,
-                "GQA group size %d not built (1 .. 16 at head_dim 128; 1, 2, 4, 8, 16 at 64)", g);
+  if (g > 16) return fail(PA_ERR_UNSUPPORTED, "GQA group size %d not built (1 .. 16)", g);
   return PA_OK;
 }
 

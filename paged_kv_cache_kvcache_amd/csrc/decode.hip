@@ -448,32 +448,36 @@ __device__ __forceinline__ void compute_chunk_v(SplitState<D, G>& st, float scal
   }
 }
 
-// ---- matrix-core variant (d = 128, one kv-head per wave, up to 16 q-heads)
+// ---- matrix-core variant (one kv-head per wave, up to 16 q-heads)
 //
 // The chunk's 32 tokens go through a per-wave LDS region so that both
 // products run on v_mfma_f32_16x16x32_bf16 with the q-heads as the 16
-// columns: S^T = K Q^T, then O^T += V^T P^T. Lane (g, i) = (lane / 16,
-// lane % 16) loaded token 4u + g, elements 8i .. 8i+7, for u = 0..7. K row
-// 4g + (u & 3) of 16-token tile u >> 2 holds that token, so the S^T
-// accumulator of tile T gives lane (g, i), register c, the score of q-head i
-// for token 16T + 4c + g. Numbered that way, the 8 scores a lane holds are
-// the 8 keys of its lane group in the B operand of the P.V product, and V^T
-// is staged in the same key order (slot 8g + u holds token 4u + g), so P
-// stays in registers. Columns past G carry zero queries and are never
-// written.
+// columns: S^T = K Q^T, then O^T += V^T P^T. In the MFMA layouts lane
+// (g, i) = (lane / 16, lane % 16); the S^T accumulator of 16-token tile T
+// gives it, in register c, the score of q-head i for K row 4g + c of the
+// tile. The loads are placed so that those 8 scores (two tiles) are the 8
+// keys of lane group g in the B operand of the P.V product, and V^T is staged
+// in the same key order (slot 8g + 4T + c), so P stays in registers:
+//   d = 128: lane (r, s) = (lane / 16, lane % 16) loaded token 4u + r,
+//     elements 8s .., u = 0..7; tile u >> 2, row 4r + (u & 3), so (T, g, c)
+//     is token 16T + 4c + g;
+//   d = 64: lane (r, s) = (lane / 8, lane % 8) loaded token 8u + r, u = 0..3;
+//     tile r >> 2, row 4(r & 3) + u, so (T, g, c) is token 8c + 4T + g.
+// Columns past G carry zero queries and are never written.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
+template <int D>
 struct MfState {
-  bf16x8 qf[4];  // Q^T operand of k-step j: lane (g, i) = q-head i, elements 32j + 8g ..
-  f32x4 o[8];    // O^T tile mt: lane (g, i), register c = element 16mt + 4g + c of q-head i
-  float m;       // column i's running max (log2 units); equal in the column's 4 lanes
-  float l;       // this lane's share of column i's sum (its tokens only)
+  bf16x8 qf[D / 32];  // Q^T operand of k-step j: lane (g, i) = q-head i, elements 32j + 8g ..
+  f32x4 o[D / 16];    // O^T tile mt: lane (g, i), register c = element 16mt + 4g + c of q-head i
+  float m;            // column i's running max (log2 units); equal in the column's 4 lanes
+  float l;            // this lane's share of column i's sum (its tokens only)
 };
 
-constexpr int kMfKBytes = 2 * 16 * 256;         // two 16-token K tiles, 256-byte rows
-constexpr int kMfVRow = 80;                      // V^T row: 32 keys x 2 B, padded
-constexpr int kMfBytes = kMfKBytes + 128 * kMfVRow;  // LDS per wave
+constexpr int mf_kbytes(int D) { return 2 * 16 * 2 * D; }  // two 16-token K tiles
+constexpr int kMfVRow = 80;                                // V^T row: 32 keys x 2 B, padded
+constexpr int mf_bytes(int D) { return mf_kbytes(D) + D * kMfVRow; }  // LDS per wave
 // A column's reference max moves only when a score exceeds it by more than
 // kMfLazy in log2 units, so a weight stays below 2^8: far inside the bf16 and
 // fp32 ranges, and most chunks skip the rescale.
@@ -487,40 +491,55 @@ __device__ __forceinline__ float sum_pair_bf16(uint32_t pair, float acc) {
                                          __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
 }
 
-// LDS rows are swizzled so that every access below is free of bank
-// conflicts: K block b of row rho sits at b ^ rho; the V^T 16-byte group of
-// lane group g in row d sits at g ^ ((d >> 4) & 3).
-template <bool TAIL>
-__device__ __forceinline__ void compute_chunk_mf(MfState& st, char* lds, float scale_log2,
-                                                 int nvalid, const uint4 (&kr)[8],
-                                                 const uint4 (&vr)[8]) {
+// LDS rows are swizzled so that the accesses below are free of bank
+// conflicts (V^T writes at d = 64: two-way): K block b of row rho sits at
+// b ^ (rho mod the blocks per row); the V^T 16-byte group of lane group g in
+// row d sits at g ^ ((d >> 4) & 3).
+template <int D, bool TAIL>
+__device__ __forceinline__ void compute_chunk_mf(MfState<D>& st, char* lds, float scale_log2,
+                                                 int nvalid, const uint4 (&kr)[D / 16],
+                                                 const uint4 (&vr)[D / 16]) {
+  constexpr int U = D / 16;          // loads per chunk (32 tokens)
+  constexpr int LPT = D / 8;         // lanes per token vector (16-byte blocks per row)
+  constexpr int ROW = 2 * D;         // bytes per K row
+  constexpr int TILE = 16 * ROW;     // bytes per 16-token K tile
   const int lane = threadIdx.x % kWave;
-  const int g = lane >> 4, i = lane & 15;
-  char* vt = lds + kMfKBytes;
+  const int g = lane >> 4, i = lane & 15;      // MFMA roles
+  const int r = lane / LPT, s = lane % LPT;    // load roles: token r of an instruction, block s
+  char* vt = lds + mf_kbytes(D);
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int rho = 4 * g + (u & 3);
-    *reinterpret_cast<uint4*>(lds + (u >> 2) * 4096 + rho * 256 + ((i ^ rho) << 4)) = kr[u];
+  for (int u = 0; u < U; ++u) {
+    const int T = D == 128 ? u >> 2 : r >> 2;
+    const int rho = D == 128 ? 4 * r + (u & 3) : 4 * (r & 3) + u;
+    *reinterpret_cast<uint4*>(lds + T * TILE + rho * ROW + ((s ^ (rho & (LPT - 1))) << 4)) = kr[u];
   }
-  // V^T: dword k of the lane's group holds tokens u = 2k (low) and 2k + 1
+  // V^T: a dword holds tokens u = 2k (low) and 2k + 1 of the lane's row r
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t c[8];
+    uint32_t c[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       const uint32_t x4[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
       c[u] = x4[w];
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const uint32_t sel = e ? 0x07060302u : 0x05040100u;  // element 2w + e of both tokens
-      uint4 x;
-      x.x = __builtin_amdgcn_perm(c[1], c[0], sel);
-      x.y = __builtin_amdgcn_perm(c[3], c[2], sel);
-      x.z = __builtin_amdgcn_perm(c[5], c[4], sel);
-      x.w = __builtin_amdgcn_perm(c[7], c[6], sel);
-      const int d = 8 * i + 2 * w + e;
-      *reinterpret_cast<uint4*>(vt + d * kMfVRow + ((g ^ ((d >> 4) & 3)) << 4)) = x;
+      const int d = 8 * s + 2 * w + e;
+      if constexpr (D == 128) {  // slots 8r .. 8r+7: the whole 16-byte group
+        uint4 x;
+        x.x = __builtin_amdgcn_perm(c[1], c[0], sel);
+        x.y = __builtin_amdgcn_perm(c[3], c[2], sel);
+        x.z = __builtin_amdgcn_perm(c[5], c[4], sel);
+        x.w = __builtin_amdgcn_perm(c[7], c[6], sel);
+        *reinterpret_cast<uint4*>(vt + d * kMfVRow + ((r ^ ((d >> 4) & 3)) << 4)) = x;
+      } else {  // slots 8(r & 3) + 4(r >> 2) .. +3: half of group r & 3
+        uint2 x;
+        x.x = __builtin_amdgcn_perm(c[1], c[0], sel);
+        x.y = __builtin_amdgcn_perm(c[3], c[2], sel);
+        *reinterpret_cast<uint2*>(vt + d * kMfVRow + (((r & 3) ^ ((d >> 4) & 3)) << 4) +
+                                  8 * (r >> 2)) = x;
+      }
     }
   }
   // a wave's LDS operations execute in order: only the compiler must keep
@@ -531,19 +550,21 @@ __device__ __forceinline__ void compute_chunk_mf(MfState& st, char* lds, float s
   for (int T = 0; T < 2; ++T) {
     sc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < D / 32; ++j) {
       const bf16x8 av = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const uint4*>(lds + T * 4096 + i * 256 + (((4 * j + g) ^ i) << 4)));
+          bf16x8, *reinterpret_cast<const uint4*>(lds + T * TILE + i * ROW +
+                                                  (((4 * j + g) ^ (i & (LPT - 1))) << 4)));
       sc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, st.qf[j], sc[T], 0, 0, 0);
     }
   }
-  float sv[8];  // token 16T + 4c + g at index 4T + c
+  float sv[8];  // K row 4g + c of tile T at index 4T + c
 #pragma unroll
   for (int T = 0; T < 2; ++T)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float x = sc[T][c];
-      sv[4 * T + c] = (!TAIL || 16 * T + 4 * c + g < nvalid) ? x : -INFINITY;
+      const int t = D == 128 ? 16 * T + 4 * c + g : 8 * c + 4 * T + g;  // token in the chunk
+      sv[4 * T + c] = (!TAIL || t < nvalid) ? x : -INFINITY;
     }
   float mx = sv[0];
 #pragma unroll
@@ -557,7 +578,7 @@ __device__ __forceinline__ void compute_chunk_mf(MfState& st, char* lds, float s
     st.m = mnew;
     st.l *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) st.o[mt] *= alpha;
+    for (int mt = 0; mt < D / 16; ++mt) st.o[mt] *= alpha;
   }
   const float negm = (st.m == -INFINITY) ? 0.f : -st.m;
   float p[8];
@@ -575,7 +596,7 @@ __device__ __forceinline__ void compute_chunk_mf(MfState& st, char* lds, float s
   st.l = sum_pair_bf16(pk.w, st.l);
   const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
+  for (int mt = 0; mt < D / 16; ++mt) {
     const int d = 16 * mt + i;
     const bf16x8 av = __builtin_bit_cast(
         bf16x8, *reinterpret_cast<const uint4*>(vt + d * kMfVRow + ((g ^ (mt & 3)) << 4)));
@@ -585,23 +606,24 @@ __device__ __forceinline__ void compute_chunk_mf(MfState& st, char* lds, float s
   asm volatile("" ::: "memory");
 }
 
-// One chunk on either path: the matrix-core state takes U = 8 (a single
-// fused token is widened to a masked chunk of 8 copies).
+// One chunk on either path: the matrix-core state takes chunks of 32 tokens
+// (a single fused token is widened to a masked chunk of copies).
 template <class L, int D, int G, int U, bool TAIL, class St>
 __device__ __forceinline__ void compute_chunk(St& st, char* lds, float scale_log2, int row,
                                               int nvalid, const uint4 (&kr)[U],
                                               const uint4 (&vr)[U]) {
-  if constexpr (std::is_same<St, MfState>::value) {
-    if constexpr (U == 8) {
-      compute_chunk_mf<TAIL>(st, lds, scale_log2, nvalid, kr, vr);
+  if constexpr (std::is_same<St, MfState<D>>::value) {
+    constexpr int UM = D / 16;
+    if constexpr (U == UM) {
+      compute_chunk_mf<D, TAIL>(st, lds, scale_log2, nvalid, kr, vr);
     } else {
-      uint4 k8[8], v8[8];
+      uint4 kw[UM], vw[UM];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        k8[u] = kr[u % U];
-        v8[u] = vr[u % U];
+      for (int u = 0; u < UM; ++u) {
+        kw[u] = kr[u % U];
+        vw[u] = vr[u % U];
       }
-      compute_chunk_mf<true>(st, lds, scale_log2, nvalid, k8, v8);
+      compute_chunk_mf<D, true>(st, lds, scale_log2, nvalid, kw, vw);
     }
   } else {
     compute_chunk_v<L, D, G, U, TAIL>(st, scale_log2, row, nvalid, kr, vr);
@@ -713,18 +735,18 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
 // VS waves per workgroup share a kv-head, each with G of its q-heads (VS = 2
 // at 16 q-heads per kv-head: a wave holds at most 8); they read the same
 // K/V rows on the same CU, so the second read is served by its caches.
-// MF: the matrix-core variant (d = 128, KPW = 1, G <= 16; G = 0 takes the
-// group size from the arguments); with VS > 1 its waves take VS adjacent
-// kv-heads, one each.
+// MF: the matrix-core variant (KPW = 1, G <= 16; G = 0 takes the group
+// size from the arguments); with VS > 1 its waves take VS adjacent kv-heads,
+// one each.
 template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1, bool MF = false>
 __global__ __launch_bounds__(kWave * VS) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
 void decode_split_kernel(DecodeArgs a) {
-  static_assert(!MF || (D == 128 && KPW == 1 && G <= 16 && VS <= 4), "matrix-core geometry");
+  static_assert(!MF || (KPW == 1 && G <= 16 && VS <= 4), "matrix-core geometry");
   static_assert(MF || G > 0, "the vector path is built per group size");
   const int Gn = G ? G : a.group;  // q-heads per kv-head
   constexpr bool kPair = MF && VS > 1;  // one kv-head per wave, VS per workgroup
-  constexpr int U = MF ? 8 : unroll_for(G);
-  using S = typename std::conditional<MF, MfState, SplitState<D, (G ? G : 1)>>::type;
+  constexpr int U = MF ? D / 16 : unroll_for(G);  // matrix cores: chunks of 32 tokens
+  using S = typename std::conditional<MF, MfState<D>, SplitState<D, (G ? G : 1)>>::type;
   using L = Lanes<D, KPW>;
   constexpr int LPT = L::LPT;
   constexpr int SEG = L::SEG;
@@ -778,12 +800,12 @@ void decode_split_kernel(DecodeArgs a) {
   S st;
   char* lds = nullptr;
   if constexpr (MF) {
-    __shared__ __attribute__((aligned(16))) char mf_lds[VS * kMfBytes];
-    lds = mf_lds + half * kMfBytes;
+    __shared__ __attribute__((aligned(16))) char mf_lds[VS * mf_bytes(D)];
+    lds = mf_lds + half * mf_bytes(D);
     // lane (g, i): q-head i (zeros past G), elements 32j + 8g .. +8
     const int qg = lane >> 4, qi = lane & 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < D / 32; ++j) {
       uint4 t = make_uint4(0, 0, 0, 0);
       if (qi < Gn) t = *reinterpret_cast<const uint4*>(a.q + (head0 + qi) * D + 32 * j + 8 * qg);
       st.qf[j] = __builtin_bit_cast(bf16x8, t);
@@ -791,7 +813,7 @@ void decode_split_kernel(DecodeArgs a) {
     st.m = -INFINITY;
     st.l = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < D / 16; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   } else {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -929,7 +951,7 @@ void decode_split_kernel(DecodeArgs a) {
         const float inv = 1.f / lt;
         uint16_t* dst = a.out + (head0 + li) * D + 4 * lg;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
+        for (int mt = 0; mt < D / 16; ++mt) {
           uint2 v;
           v.x = pack_bf16x2(st.o[mt][0] * inv, st.o[mt][1] * inv);
           v.y = pack_bf16x2(st.o[mt][2] * inv, st.o[mt][3] * inv);
@@ -939,7 +961,7 @@ void decode_split_kernel(DecodeArgs a) {
         const int64_t wi = (head0 + li) * a.max_parts + part;
         float* dst = a.ws_o + wi * D + 4 * lg;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int mt = 0; mt < D / 16; ++mt)
           *reinterpret_cast<float4*>(dst + 16 * mt) =
               make_float4(st.o[mt][0], st.o[mt][1], st.o[mt][2], st.o[mt][3]);
         if (lg == 0) *reinterpret_cast<float2*>(a.ws_ml + wi * 2) = make_float2(st.m, lt);
@@ -1052,34 +1074,32 @@ SplitFn pick_split(int G) {
   return nullptr;
 }
 
-// The matrix-core variant (d = 128, one kv-head per wave, VS waves per
-// workgroup).
-template <bool FUSED, bool SMALL, bool DRAIN, int VS>
+// The matrix-core variant (one kv-head per wave, VS waves per workgroup):
+// group sizes 8 and 16 built as such, the others (up to 16) take G from the
+// arguments.
+template <int D, bool FUSED, bool SMALL, bool DRAIN, int VS>
 SplitFn pick_split_mf(int G) {
   constexpr bool kD = DRAIN && !SMALL;
   switch (G) {
-    case 1: return decode_split_kernel<128, 1, 1, FUSED, SMALL, kD, VS, true>;
-    case 2: return decode_split_kernel<128, 2, 1, FUSED, SMALL, kD, VS, true>;
-    case 4: return decode_split_kernel<128, 4, 1, FUSED, SMALL, kD, VS, true>;
-    case 8: return decode_split_kernel<128, 8, 1, FUSED, SMALL, kD, VS, true>;
-    case 16: return decode_split_kernel<128, 16, 1, FUSED, SMALL, kD, VS, true>;
+    case 8: return decode_split_kernel<D, 8, 1, FUSED, SMALL, kD, VS, true>;
+    case 16: return decode_split_kernel<D, 16, 1, FUSED, SMALL, kD, VS, true>;
   }
-  return G >= 1 && G <= 16 ? decode_split_kernel<128, 0, 1, FUSED, SMALL, kD, VS, true> : nullptr;
+  return G >= 1 && G <= 16 ? decode_split_kernel<D, 0, 1, FUSED, SMALL, kD, VS, true> : nullptr;
 }
 
-template <bool FUSED, int VS>
+template <int D, bool FUSED, int VS>
 SplitFn pick_split_mf(int G, bool small, bool drain) {
-  if (small) return pick_split_mf<FUSED, true, false, VS>(G);
-  return drain ? pick_split_mf<FUSED, false, true, VS>(G)
-               : pick_split_mf<FUSED, false, false, VS>(G);
+  if (small) return pick_split_mf<D, FUSED, true, false, VS>(G);
+  return drain ? pick_split_mf<D, FUSED, false, true, VS>(G)
+               : pick_split_mf<D, FUSED, false, false, VS>(G);
 }
 
-template <bool FUSED>
+template <int D, bool FUSED>
 SplitFn pick_split_mf(int G, bool small, bool drain, int waves) {
   switch (waves) {
-    case 1: return pick_split_mf<FUSED, 1>(G, small, drain);
-    case 2: return pick_split_mf<FUSED, 2>(G, small, drain);
-    case 4: return pick_split_mf<FUSED, 4>(G, small, drain);
+    case 1: return pick_split_mf<D, FUSED, 1>(G, small, drain);
+    case 2: return pick_split_mf<D, FUSED, 2>(G, small, drain);
+    case 4: return pick_split_mf<D, FUSED, 4>(G, small, drain);
   }
   return nullptr;
 }
@@ -1110,10 +1130,14 @@ SplitFn pick_split(int G, bool fused, bool small, bool drain) {
 #ifndef PA_DECODE_MF_MIN_G
 #define PA_DECODE_MF_MIN_G 8
 #endif
-// Group sizes from PA_DECODE_MF_MIN_G up, and those that are not powers of
-// two, run on the matrix cores at d = 128.
+#ifndef PA_DECODE_MF64_MIN_G
+#define PA_DECODE_MF64_MIN_G 8
+#endif
+// Group sizes from PA_DECODE_MF_MIN_G (d = 128) or PA_DECODE_MF64_MIN_G
+// (d = 64) up, and those that are not powers of two, run on the matrix cores.
 bool mf_group(int head_dim, int G) {
-  return head_dim == 128 && (G >= PA_DECODE_MF_MIN_G || (G & (G - 1)) != 0);
+  const int min_g = head_dim == 128 ? PA_DECODE_MF_MIN_G : PA_DECODE_MF64_MIN_G;
+  return G >= min_g || (G & (G - 1)) != 0;
 }
 bool use_mf(const pa_desc* d) { return mf_group(d->head_dim, d->num_q_heads / d->num_kv_heads); }
 #ifndef PA_DECODE_MF_GROUP
@@ -1292,7 +1316,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
 
   hipStream_t s = (hipStream_t)stream;
   const bool mf = use_mf(desc);
-  const int chunk = (kWave / (D / 8 * kpw)) * (mf ? 8 : unroll_for(min(G, 8)));  // tokens per chunk
+  const int chunk = mf ? 32 : (kWave / (D / 8 * kpw)) * unroll_for(min(G, 8));  // tokens per chunk
   const bool small = desc->block_size < chunk;
   const bool fused = nt != nullptr;
   // the wave slots are full (2 per SIMD): one chunk of loads in flight per wave
@@ -1300,8 +1324,12 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   SplitFn split = nullptr;
   if (mf) {
     const int waves = mf_waves(desc);
-    split = fused ? pick_split_mf<true>(G, small, drain, waves)
-                  : pick_split_mf<false>(G, small, drain, waves);
+    if (D == 128)
+      split = fused ? pick_split_mf<128, true>(G, small, drain, waves)
+                    : pick_split_mf<128, false>(G, small, drain, waves);
+    else
+      split = fused ? pick_split_mf<64, true>(G, small, drain, waves)
+                    : pick_split_mf<64, false>(G, small, drain, waves);
   } else if (D == 128) {
     split = kpw == 2 ? pick_split<128, 2>(G, fused, small, drain)
                      : pick_split<128, 1>(G, fused, small, drain);

@@ -433,9 +433,7 @@ PrefillFn pick(int G) {
     case 8: return prefill_kernel<D, 8, SMALL>;
     case 16: return prefill_kernel<D, 16, SMALL>;
   }
-  // other group sizes (head_dim 128 only)
-  if constexpr (D == 128) return G >= 1 && G <= kTiles ? prefill_kernel<D, 0, SMALL> : nullptr;
-  return nullptr;
+  return G >= 1 && G <= kTiles ? prefill_kernel<D, 0, SMALL> : nullptr;  // other group sizes
 }
 
 }  // namespace

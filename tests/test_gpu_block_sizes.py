@@ -58,7 +58,8 @@ def test_store_and_decode(bsz, h_q, h_kv, d):
 
 
 @pytest.mark.parametrize("bsz", [16, 64, 1024])
-@pytest.mark.parametrize("h_q,h_kv,d", [(32, 8, 128), (16, 4, 64), (64, 4, 128), (40, 8, 128)])
+@pytest.mark.parametrize("h_q,h_kv,d", [(32, 8, 128), (16, 4, 64), (64, 4, 128), (40, 8, 128),
+                                         (32, 4, 64)])
 def test_fused_step(bsz, h_q, h_kv, d):
     case = W.decode_case(h_q, h_kv, d, LENS, seed=95 + bsz, block_size=bsz)
     print("block size %d fused step" % bsz, flush=True)

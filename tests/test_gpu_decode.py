@@ -121,16 +121,16 @@ def test_ctx1_returns_value_bit_exact():
 
 # covers every lane layout: one kv-head per wave (d 64 with 1 or 2 kv-heads,
 # d 128 with an odd head count), two per wave (d 128), four per wave (d 64
-# with a multiple of 4 kv-heads), two waves per kv-head (d 64, group size
-# 16), and the matrix cores at d 128 for group sizes 8 and 16 and those that
-# are not powers of two (3, 5, 6, 7, 12; odd kv-head counts take one wave
-# per workgroup)
+# with a multiple of 4 kv-heads), and the matrix cores at both head dims for
+# group sizes 8 and 16 and those that are not powers of two (3, 5, 6, 7, 12;
+# odd kv-head counts take one wave per workgroup)
 @pytest.mark.parametrize("h_q,h_kv,d", [(8, 8, 128), (16, 8, 128), (32, 4, 128), (4, 2, 64),
                                          (16, 2, 64), (8, 1, 64), (12, 3, 128), (64, 8, 128),
                                          (16, 4, 64), (32, 8, 64), (8, 8, 64), (64, 8, 64),
                                          (64, 4, 128), (32, 2, 64), (16, 1, 128), (40, 8, 128),
                                          (28, 4, 128), (12, 2, 128), (24, 8, 128), (36, 3, 128),
-                                         (15, 3, 128)])
+                                         (15, 3, 128), (14, 2, 64), (15, 5, 64), (48, 4, 64),
+                                         (40, 8, 64)])
 def test_group_sizes_and_head_dims_with_ragged_tails(h_q, h_kv, d):
     lens = [1, 2, 31, 32, 33, 255, 256, 257, 511, 513, 1000, 2049]
     case = W.decode_case(h_q, h_kv, d, lens, seed=72 + h_q + d)

@@ -87,7 +87,7 @@ def ragged_case(h_q, h_kv, d, prefix, suffix, seed):
 @pytest.mark.parametrize("h_q,h_kv,d", [(32, 8, 128), (8, 8, 128), (16, 8, 128), (64, 8, 128),
                                          (4, 2, 64), (8, 1, 64), (16, 2, 64), (64, 4, 128),
                                          (16, 1, 64), (40, 8, 128), (28, 4, 128), (12, 1, 128),
-                                         (24, 8, 128), (18, 3, 128)])
+                                         (24, 8, 128), (18, 3, 128), (14, 2, 64), (15, 5, 64)])
 def test_small_cases_full_oracle(h_q, h_kv, d):
     """Ragged q lengths (1, < 16, not multiples of the tile), cached prefixes
     that end mid-block (chunked prefill), no prefix, poisoned unused rows."""

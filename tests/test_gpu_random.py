@@ -30,7 +30,7 @@ def _shape(rng):
     g = int(rng.choice([1, 2, 4, 8, 16]))
     h_kv = int(rng.choice([1, 2, 3, 4, 8]))
     bsz = int(rng.choice([16, 32, 64, 128, 256, 512, 1024]))
-    if d == 128 and rng.random() < 0.3:  # group sizes that are not powers of two
+    if rng.random() < 0.3:  # group sizes that are not powers of two
         g = int(rng.choice([3, 5, 6, 7, 12]))
     return g * h_kv, h_kv, d, bsz
 

@@ -58,17 +58,18 @@ def test_host_argument_checks_need_no_gpu(lib):
     assert lib.pa_decode(None, None, None, None, 0, None, 1, 0, 1.0, None, None, 0,
                          ctypes.byref(bad), None) == B.PA_ERR_INVALID_ARG
     assert b"multiple" in lib.pa_last_error()
-    for kw in (dict(d=96), dict(bsz=8), dict(bsz=48), dict(bsz=2048), dict(h_q=24, h_kv=2, d=64),
-               dict(h_q=64, h_kv=2), dict(h_q=34, h_kv=2)):  # group sizes 12 (d 64), 32, 17
+    for kw in (dict(d=96), dict(bsz=8), dict(bsz=48), dict(bsz=2048), dict(h_q=64, h_kv=2),
+               dict(h_q=34, h_kv=2), dict(h_q=34, h_kv=2, d=64)):  # group sizes 32, 17
         assert lib.pa_decode(None, None, None, None, 0, None, 1, 0, 1.0, None, None, 0,
                              ctypes.byref(_desc(**kw)), None) == B.PA_ERR_UNSUPPORTED
     for bsz in (16, 32, 64, 128, 512, 1024):  # every built block size: an empty batch is a no-op
         assert lib.pa_decode(None, None, None, None, 0, None, 0, 0, 1.0, None, None, 0,
                              ctypes.byref(_desc(bsz=bsz)), None) == 0
     for h_q, h_kv in ((8, 8), (16, 8), (32, 8), (64, 8), (64, 4), (24, 8), (40, 8), (28, 4),
-                      (24, 2)):  # group sizes 1 .. 16 at d 128, powers of two or not
-        assert lib.pa_decode(None, None, None, None, 0, None, 0, 0, 1.0, None, None, 0,
-                             ctypes.byref(_desc(h_q=h_q, h_kv=h_kv)), None) == 0
+                      (24, 2)):  # group sizes 1 .. 16, powers of two or not
+        for d_ in (64, 128):
+            assert lib.pa_decode(None, None, None, None, 0, None, 0, 0, 1.0, None, None, 0,
+                                 ctypes.byref(_desc(h_q=h_q, h_kv=h_kv, d=d_)), None) == 0
     assert lib.pa_decode(None, None, None, None, 0, None, 0, 0, 1.0, None, None, 0,
                          ctypes.byref(d), None) == 0  # empty batch: no-op
     # workspace checked before any launch
