@@ -1022,29 +1022,61 @@ void decode_split_kernel(DecodeArgs a) {
 
 // Exact log-sum-exp merge of a sequence's partitions:
 // M = max m_p, L = sum l_p 2^(m_p - M), out = sum o_p 2^(m_p - M) / L.
+// One wave per (sequence, q-head), kReduceWaves per workgroup (4 measured
+// no faster than 1). The partitions are read kReduceParts at a time (one
+// round of loads for up to that many) and folded into a running max, so a
+// merge of up to kReduceParts partitions waits for memory once after the
+// length (against two passes over the partitions: 32 x 16,384 tokens
+// 336 -> 327 us per call, Qwen3-0.6B batch 87.6 -> 84.4 us).
+#ifndef PA_DECODE_REDUCE_WAVES
+#define PA_DECODE_REDUCE_WAVES 1
+#endif
+constexpr int kReduceWaves = PA_DECODE_REDUCE_WAVES;
+constexpr int kReduceParts = 8;
+
 template <int D>
-__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a, int H_q) {
+__global__ __launch_bounds__(kWave * kReduceWaves) void decode_reduce_kernel(DecodeArgs a,
+                                                                              int H_q) {
   constexpr int EPL = D / kWave;  // output elements per lane
-  const int h = blockIdx.x % H_q;
-  const int b = blockIdx.x / H_q;
+  const int hg = (H_q + kReduceWaves - 1) / kReduceWaves;  // workgroups per sequence
+  const int h = (blockIdx.x % hg) * kReduceWaves + threadIdx.x / kWave;
+  const int b = blockIdx.x / hg;
+  if (h >= H_q) return;
   const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
   const int nparts = split_parts(n, a.part_tokens, a.max_parts).k;
   if (nparts <= 1) return;
   const int64_t w0 = ((int64_t)b * H_q + h) * a.max_parts;
-  const int lane = threadIdx.x;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, a.ws_ml[(w0 + p) * 2]);
-  float L = 0.f;
+  const int lane = threadIdx.x % kWave;
+  float M = -INFINITY, L = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float2 ml = *reinterpret_cast<const float2*>(a.ws_ml + (w0 + p) * 2);
-    const float w = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - M);
-    L = fmaf(ml.y, w, L);
-    const float* src = a.ws_o + (w0 + p) * D + lane * EPL;
+  for (int p0 = 0; p0 < nparts; p0 += kReduceParts) {
+    float2 ml[kReduceParts];
+    float src[kReduceParts][EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = fmaf(src[e], w, o[e]);
+    for (int k = 0; k < kReduceParts; ++k) {
+      const int p = min(p0 + k, nparts - 1);  // past the last: re-read it, weight 0 below
+      ml[k] = *reinterpret_cast<const float2*>(a.ws_ml + (w0 + p) * 2);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) src[k][e] = a.ws_o[(w0 + p) * D + lane * EPL + e];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < kReduceParts; ++k)
+      if (p0 + k < nparts) Mc = fmaxf(Mc, ml[k].x);
+    const float r = (M == -INFINITY) ? 0.f : exp2f(M - Mc);  // rescale what came before
+    L *= r;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] *= r;
+#pragma unroll
+    for (int k = 0; k < kReduceParts; ++k) {
+      const float w = (p0 + k >= nparts || ml[k].x == -INFINITY) ? 0.f : exp2f(ml[k].x - Mc);
+      L = fmaf(ml[k].y, w, L);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(src[k][e], w, o[e]);
+    }
+    M = Mc;
   }
   const float inv = 1.f / L;
   uint16_t* dst = a.out + ((int64_t)b * H_q + h) * D + lane * EPL;
@@ -1351,13 +1383,14 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   rc = launch_status(who);
   if (rc) return rc;
   if (plan.max_parts > 1) {
-    const unsigned rows = (unsigned)num_seqs * desc->num_q_heads;
+    const unsigned wgs =
+        (unsigned)num_seqs * ((desc->num_q_heads + kReduceWaves - 1) / kReduceWaves);
     if (D == 128)
-      hipLaunchKernelGGL(decode_reduce_kernel<128>, dim3(rows), dim3(kWave), 0, s, a,
-                         desc->num_q_heads);
+      hipLaunchKernelGGL(decode_reduce_kernel<128>, dim3(wgs), dim3(kWave * kReduceWaves), 0, s,
+                         a, desc->num_q_heads);
     else
-      hipLaunchKernelGGL(decode_reduce_kernel<64>, dim3(rows), dim3(kWave), 0, s, a,
-                         desc->num_q_heads);
+      hipLaunchKernelGGL(decode_reduce_kernel<64>, dim3(wgs), dim3(kWave * kReduceWaves), 0, s,
+                         a, desc->num_q_heads);
     rc = launch_status(who);
     if (rc) return rc;
   }

@@ -500,6 +500,7 @@ int launch_prefill(const char* who, const void* q, const void* k_cache, const vo
   const bool small = desc->block_size < kKT;
   PrefillFn fn = D == 128 ? (small ? pick<128, true>(G) : pick<128, false>(G))
                           : (small ? pick<64, true>(G) : pick<64, false>(G));
+  if (!fn) return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for group size %d", who, G);
   hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream, a);
   return launch_status(who);
 }
