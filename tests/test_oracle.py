@@ -164,7 +164,9 @@ def check_decode_vs_sdpa(decode_fn):
     """Identity table: paged decode == contiguous attention (library routine)."""
     for (h_q, h_kv, d, lens, seed) in [(4, 2, 64, [1, 17, 256, 300], 11),
                                        (8, 2, 128, [513, 40], 12),
-                                       (6, 6, 32, [77], 13)]:
+                                       (6, 6, 32, [77], 13),
+                                       (10, 2, 32, [40, 260], 14),    # group size 5
+                                       (21, 3, 32, [300], 15)]:       # group size 7
         kc, vc, bt = _identity_case(h_q, h_kv, d, lens, seed)
         rng = np.random.default_rng(seed + 100)
         q = W.normal_bf16(rng, (len(lens), h_q, d))
@@ -187,7 +189,8 @@ def check_prefill_vs_full_recompute(prefill_fn):
     suffix rows of full causal attention over the whole sequence (computed
     with the library routine, where q_len == k_len)."""
     for (h_q, h_kv, d, prefix, suffix, seed) in [(4, 2, 64, [256, 0, 300], [40, 5, 1], 21),
-                                                 (8, 2, 128, [512], [300], 22)]:
+                                                 (8, 2, 128, [512], [300], 22),
+                                                 (6, 2, 32, [100], [60], 23)]:  # group size 3
         ends = [p + s for p, s in zip(prefix, suffix)]
         kc, vc, bt = _identity_case(h_q, h_kv, d, ends, seed)
         rng = np.random.default_rng(seed + 100)
