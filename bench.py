@@ -30,6 +30,11 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 LAYERS_QWEN3_8B = 36
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_decode_qwen3-8b.json")
+
+
+def pmc_decode_file(config: str) -> str:
+    """The committed counter record of a decode workload (may not exist)."""
+    return os.path.join(ROOT, "profiles", "pmc_decode_%s.json" % config)
 PMC_PREFILL_FILE = os.path.join(ROOT, "profiles", "pmc_prefill_prefix1024.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_kvcache_amd", "csrc", "decode.hip")
 PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_kvcache_amd", "csrc", "prefill.hip")
@@ -433,7 +438,8 @@ def main() -> int:
         dom, dom_bytes = "pa_decode", db
         dom_desc = "pa_decode (order + split-K + merge)"
     dom_gbs = dom_bytes / (ms_call[dom] * 1e-3) / 1e9
-    traffic = traffic_from_profile(PMC_FILE, DECODE_SRC, args.mode, args.block_size, args.config)
+    traffic = traffic_from_profile(pmc_decode_file(args.config), DECODE_SRC, args.mode,
+                                   args.block_size, args.config)
 
     rec = {
         "metric": "paged decode: KV GB/s (% HBM peak) + tokens/s at Qwen3-8B shape, batch 256",

@@ -43,7 +43,8 @@ def test_source_digest_ignores_comments(tmp_path):
     assert bench.src_hash(str(a)) != bench.src_hash(str(b))
 
 
-def test_committed_decode_record_names_its_workload():
-    rec = json.load(open(bench.PMC_FILE))
-    assert rec["config"] == "qwen3-8b" and rec["step_mode"] == "separate"
-    assert rec["block_size"] == 256 and rec["traffic_bytes_per_launch"] > 0
+def test_committed_decode_records_name_their_workloads():
+    for config in ("qwen3-8b", "gqa8", "gqa16"):
+        rec = json.load(open(bench.pmc_decode_file(config)))
+        assert rec["config"] == config and rec["step_mode"] == "separate"
+        assert rec["block_size"] == 256 and rec["traffic_bytes_per_launch"] > 0
