@@ -48,3 +48,11 @@ def test_committed_decode_records_name_their_workloads():
         rec = json.load(open(bench.pmc_decode_file(config)))
         assert rec["config"] == config and rec["step_mode"] == "separate"
         assert rec["block_size"] == 256 and rec["traffic_bytes_per_launch"] > 0
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and r.stdout == ""
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
