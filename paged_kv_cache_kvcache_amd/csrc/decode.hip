@@ -732,9 +732,10 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
 // A work item is (sequence, group of KPW adjacent kv-heads, partition).
 // SMALL: blocks hold fewer tokens than a chunk, so each load group looks up
 // its own block; otherwise a chunk lies inside one block.
-// VS waves per workgroup share a kv-head, each with G of its q-heads (VS = 2
-// at 16 q-heads per kv-head: a wave holds at most 8); they read the same
-// K/V rows on the same CU, so the second read is served by its caches.
+// Vector path: VS waves per workgroup share a kv-head, each with G of its
+// q-heads (VS = 2 at 16 q-heads per kv-head: a wave holds at most 8); they
+// read the same K/V rows on the same CU, so the second read is served by its
+// caches.
 // MF: the matrix-core variant (KPW = 1, G <= 16; G = 0 takes the group
 // size from the arguments); with VS > 1 its waves take VS adjacent kv-heads,
 // one each.
