@@ -194,11 +194,13 @@ def test_prefill_store_bit_exact():
 
 
 @pytest.mark.parametrize("batch,h_q,h_kv,d", [(1536, 32, 8, 128), (1536, 64, 8, 128),
-                                              (4096, 8, 2, 64), (4097, 8, 2, 64)])
+                                              (4096, 8, 2, 64), (4097, 8, 2, 64),
+                                              (4097, 16, 2, 64)])
 def test_large_batch_of_short_sequences(batch, h_q, h_kv, d):
     """Large batches of short sequences: up to 4,096 sequences the items are
     ranked by the order kernel (sequence ids fill its 12 bits at 4,096), one
-    more keeps the plain dispatch order (highest partition first). Lengths
+    more keeps the plain dispatch order (highest partition first), on the
+    vector path and (16 q / 2 kv heads) the matrix cores. Lengths
     1..600 with a few padding rows; sampled rows and every padding row vs the
     oracle."""
     rng = np.random.default_rng(77 + batch)
