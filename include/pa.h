@@ -87,10 +87,12 @@ int pa_store_kv(const void* k, int64_t k_row_stride, const void* v, int64_t v_ro
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for
  * this batch geometry: split-K partial results when a sequence can span
- * more than one partition, and a longest-first dispatch order when the
- * grid has more work items than the GPU has compute units (at most 4096
- * sequences). 0 when neither applies, and on invalid arguments. The result
- * depends only on the arguments.
+ * more than one partition, and a longest-first dispatch order (with the
+ * partition length chosen on the device from the actual lengths, never
+ * shorter than the host's estimate) when the grid has more work items than
+ * the GPU has compute units (at most 4096 sequences). 0 when neither
+ * applies, and on invalid arguments. The result depends only on the
+ * arguments.
  */
 size_t pa_decode_workspace_size(const pa_desc* desc, int32_t num_seqs, int32_t max_context_len);
 
@@ -132,9 +134,11 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
 /*
  * pa_decode_partitioned -- pa_decode with an explicit split-K partition of
  * partition_blocks * 256 tokens per work item, whatever block_size is (whole
- * blocks at block_size 256; 0 = the library's choice,
- * which is what pa_decode uses). The result is the same attention for any
- * partition size up to rounding. Workspace: pa_decode_workspace_size_ex.
+ * blocks at block_size 256; 0 = the library's choice, which is what pa_decode
+ * uses: estimated on the host from max_context_len, and lengthened on the
+ * device from the actual lengths when the dispatch order is computed). The
+ * result is the same attention for any partition size up to rounding.
+ * Workspace: pa_decode_workspace_size_ex.
  */
 int pa_decode_partitioned(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -81,6 +81,8 @@ struct DecodeArgs {
   int32_t block_size;   // tokens per physical block (power of two)
   int32_t block_shift;  // log2(block_size)
   int32_t* order;  // dispatch order (decode_order_kernel), or null: plain order
+  // partition length chosen by decode_order_kernel (null: part_tokens)
+  int32_t* part_dev;
   int32_t group;   // q-heads per kv-head
   float scale_log2;
 };
@@ -120,6 +122,15 @@ __device__ __forceinline__ Parts split_parts(int n, int P, int max_parts) {
   r.n = min(n, max_parts * P);
   r.k = (r.n + P - 1) / P;
   return r;
+}
+
+// Partition lengths are counted in units of 256 tokens, whatever the block size.
+constexpr int kPartUnit = 256;
+
+// Tokens per partition of this call: the host's, or the order kernel's
+// choice when it ran (never shorter than the host's, so never more parts).
+__device__ __forceinline__ int part_tokens(const DecodeArgs& a) {
+  return a.part_dev ? __builtin_amdgcn_readfirstlane(*a.part_dev) : a.part_tokens;
 }
 
 // Byte offset in a cache of token `pos` of a sequence, given the table entry
@@ -638,7 +649,8 @@ __device__ __forceinline__ void compute_chunk(St& st, char* lds, float scale_log
 // full partitions in the top one; empty sequences, which only write zeros,
 // last). One workgroup ranks them before the split kernel runs (a histogram
 // of the buckets, then each item takes the next rank of its bucket) and
-// writes order[slot] = (part << 12) | sequence, -1 past the last item (slot:
+// writes order[slot] = (P / 256) << 24 | part << 12 | sequence (P: the
+// partition length it chose), -1 past the last item (slot:
 // the rank laid out by dispatch_slot); a split wave reads its one entry. (Each wave ranking
 // the items itself from the lengths cost it 8-24 us: every wave read the
 // same lengths.)
@@ -672,17 +684,68 @@ __device__ __forceinline__ int dispatch_slot(int r, int round, int max_items) {
 #endif
 }
 
+// PartRule: the host's partition heuristic (default_partition_blocks), which
+// estimates the mean length as half the longest; the order kernel reads
+// every length and applies it to the true mean. auto_units = 0: the caller
+// fixed the partition length.
+struct PartRule {
+  int auto_units;  // longest partition tried, in units of 256 tokens (0: keep the host's)
+  int waves;       // waves per sequence and partition
+  int fill;        // waves that count as filling the chip
+};
+
 __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs a, int max_items,
-                                                                     int round) {
+                                                                     int round, PartRule rule) {
   constexpr int NB = kOrderBuckets + 1;
   __shared__ int next[NB];  // counts, then the next free rank of each bucket
   __shared__ int total;
+  // each length read once from memory (the host orders at most this many)
+  __shared__ int lens[PA_DECODE_ORDER_MAX_SEQS > 0 ? PA_DECODE_ORDER_MAX_SEQS : 1];
+  __shared__ unsigned long long sum_len;
+  __shared__ int chosen;
   const int t = threadIdx.x;
-  const int P = a.part_tokens;
+  if (t == 0) sum_len = 0;
+  __syncthreads();
+  unsigned long long mine = 0;
+  for (int s = t; s < a.num_seqs; s += kOrderThreads) {
+    const int n = clamp_len(seq_len(a, s), a.max_blocks, a.block_size);
+    lens[s] = n;
+    mine += (unsigned long long)n;
+  }
+  if (rule.auto_units > 0) {
+    // one LDS atomic per wave
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) mine += __shfl_xor(mine, off, kWave);
+    if (t % kWave == 0 && mine) atomicAdd(&sum_len, mine);
+  }
+  __syncthreads();
+  if (t == 0) {
+    // the longest partition whose item count still fills the chip, never
+    // shorter than the host's (the workspace holds max_parts partitions of
+    // the host's length)
+    int P = a.part_tokens;
+    if (rule.auto_units > 0) {
+      const double mean = fmax(1.0, floor((double)sum_len / a.num_seqs));
+      int units = 1;
+      for (int u = rule.auto_units; u > 1; u >>= 1) {
+        const double per_seq = ceil(mean / (u * kPartUnit));
+        if ((double)a.num_seqs * rule.waves * per_seq >= rule.fill) {
+          units = u;
+          break;
+        }
+      }
+      P = max(P, units * kPartUnit);
+    }
+    chosen = P;
+    *a.part_dev = P;
+  }
+  __syncthreads();
+  const int P = chosen;
+  const int tag = (P / kPartUnit) << 24;  // the partition length travels with every entry
   // a sequence's items: `bulk` full partitions in bucket kb (the top one),
   // then its last part in bucket kl (an empty sequence: one item, in bucket 0)
   auto items = [&](int s, int& bulk, int& kb, int& kl) {
-    const int n = clamp_len(seq_len(a, s), a.max_blocks, a.block_size);
+    const int n = lens[s];
     if (n == 0) {
       bulk = 0;
       kb = 0;
@@ -721,9 +784,10 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
     items(s, bulk, kb, kl);
     if (bulk) {
       const int pos = atomicAdd(&next[kb], bulk);
-      for (int j = 0; j < bulk; ++j) order[dispatch_slot(pos + j, round, max_items)] = (j << 12) | s;
+      for (int j = 0; j < bulk; ++j)
+        order[dispatch_slot(pos + j, round, max_items)] = tag | (j << 12) | s;
     }
-    order[dispatch_slot(atomicAdd(&next[kl], 1), round, max_items)] = (bulk << 12) | s;
+    order[dispatch_slot(atomicAdd(&next[kl], 1), round, max_items)] = tag | (bulk << 12) | s;
   }
   for (int r = total + t; r < max_items; r += kOrderThreads)
     order[dispatch_slot(r, round, max_items)] = -1;
@@ -760,13 +824,14 @@ void decode_split_kernel(DecodeArgs a) {
   // kv-head groups (the host checks divisibility)
   const int n_groups = H_kv / (kPair ? VS : KPW);
   const int gw = blockIdx.x % n_groups;  // the kv-head groups of one item are adjacent
-  int b, part;
+  int b, part, P = a.part_tokens;  // P: tokens per partition
   if (a.order) {
     // items longest first (decode_order_kernel)
     const int v = a.order[blockIdx.x / n_groups];
     if (v < 0) return;
     b = __builtin_amdgcn_readfirstlane(v & 4095);
-    part = __builtin_amdgcn_readfirstlane(v >> 12);
+    part = __builtin_amdgcn_readfirstlane((v >> 12) & 4095);
+    P = __builtin_amdgcn_readfirstlane((v >> 24) * kPartUnit);
   } else {
     // highest partition first
     const int idx = blockIdx.x / n_groups;
@@ -781,7 +846,7 @@ void decode_split_kernel(DecodeArgs a) {
   const int row = lane / SEG;                 // which token of a load instruction
 
   const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
-  const Parts parts = split_parts(n, a.part_tokens, a.max_parts);
+  const Parts parts = split_parts(n, P, a.max_parts);
   const int64_t head0 = kPair ? (int64_t)b * H_q + (int64_t)g * Gn
                               : (int64_t)b * H_q + (int64_t)g * Gn * VS + half * Gn;  // first q-head
 
@@ -794,8 +859,8 @@ void decode_split_kernel(DecodeArgs a) {
     return;
   }
   if (part >= parts.k) return;
-  const int start = part * a.part_tokens;
-  const int end = min(parts.n, start + a.part_tokens);
+  const int start = part * P;
+  const int end = min(parts.n, start + P);
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
 
   S st;
@@ -1044,7 +1109,7 @@ __global__ __launch_bounds__(kWave * kReduceWaves) void decode_reduce_kernel(Dec
   const int b = blockIdx.x / hg;
   if (h >= H_q) return;
   const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
-  const int nparts = split_parts(n, a.part_tokens, a.max_parts).k;
+  const int nparts = split_parts(n, part_tokens(a), a.max_parts).k;
   if (nparts <= 1) return;
   const int64_t w0 = ((int64_t)b * H_q + h) * a.max_parts;
   const int lane = threadIdx.x % kWave;
@@ -1204,8 +1269,6 @@ int item_groups(const pa_desc* d) {
   return d->num_kv_heads / kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
 }
 
-// Partition lengths are counted in units of 256 tokens, whatever the block size.
-constexpr int kPartUnit = 256;
 
 // Resident work items the split kernel keeps on an MI355X: 256 CUs x 8 waves.
 // A fixed constant (not a device query) so the workspace size is a pure
@@ -1213,33 +1276,43 @@ constexpr int kPartUnit = 256;
 constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kResidentItems = kComputeUnits * 8;
 
-// Longest partition (16 (multi-head waves and the matrix-core variant only),
-// 8, 4, 2 or 1 units of 256 tokens) whose wave count still fills half the
-// resident slots, estimating
-// the mean context as max_context_len / 2. Long partitions amortise each
-// item's set-up and keep its loads streaming (fewer concurrent streams also
-// read HBM more efficiently); short ones keep small batches spread over the
-// whole chip.
+// Longest partition (16, 8, 4, 2 or 1 units of 256 tokens) whose wave count
+// still fills the chip, estimating the mean context as max_context_len / 2
+// (the order kernel, when it runs, applies the same rule to the true mean
+// and may lengthen the partitions). Long partitions amortise each item's
+// set-up and keep its loads streaming (fewer concurrent streams also read
+// HBM more efficiently); short ones keep small batches spread over the whole
+// chip.
+// The heuristic's inputs: longest partition tried (16 units for multi-head
+// waves and the matrix-core variant, else 8), waves per sequence and
+// partition (a matrix-core item is one wave per kv-head), and the waves that
+// count as filling the chip (matrix-core items of two waves keep long
+// partitions down to a quarter of the slots: 64 q / 8 kv heads at batch 64,
+// 186 us with 4,096 tokens, 195 us with 2,048).
+PartRule part_rule(const pa_desc* d) {
+  const int kpw = kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
+  const bool mf = use_mf(d);
+  PartRule r;
+  r.auto_units = (kpw > 1 || mf) ? 16 : 8;
+  r.waves = mf ? d->num_kv_heads : item_groups(d);
+  r.fill = (int)(mf && mf_waves(d) > 1 ? kResidentItems / 4 : kResidentItems / 2);
+  return r;
+}
+
 int default_partition_blocks(const pa_desc* d, int32_t num_seqs, int32_t max_ctx) {
   const int64_t mean_ctx = max(1, max_ctx / 2);
-  const int kpw = kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
-  // waves per sequence and partition (a matrix-core item is one per kv-head);
-  // matrix-core items of two waves keep long partitions down to a quarter
-  // of the slots (64 q / 8 kv heads at batch 64: 186 us with 4,096 tokens,
-  // 195 us with 2,048)
-  const bool mf = use_mf(d);
-  const int groups = mf ? d->num_kv_heads : item_groups(d);
-  const int64_t fill = mf && mf_waves(d) > 1 ? kResidentItems / 4 : kResidentItems / 2;
-  for (int p = (kpw > 1 || mf) ? 16 : 8; p > 1; p >>= 1) {
+  const PartRule r = part_rule(d);
+  for (int p = r.auto_units; p > 1; p >>= 1) {
     const int64_t per_seq = (mean_ctx + (int64_t)p * kPartUnit - 1) / ((int64_t)p * kPartUnit);
-    if ((int64_t)num_seqs * groups * per_seq >= fill) return p;
+    if ((int64_t)num_seqs * r.waves * per_seq >= r.fill) return p;
   }
   return 1;
 }
 
 // Workspace: the partitions' (o[d], m, l) fp32 partials when a sequence can
 // span more than one partition, then the dispatch order (one int32 per
-// sequence and partition) when the grid has more items than CUs. The order
+// sequence and partition, 16-byte rounded) and the partition length the
+// order kernel chose (16 bytes) when the grid has more items than CUs. The order
 // matters even when every item is resident at once: a CU's share of HBM
 // bandwidth is bounded, and longest first deals the long items out across
 // the CUs instead of stacking some on a few.
@@ -1247,21 +1320,28 @@ struct Plan {
   int part_tokens;
   int max_parts;
   bool ordered;
+  bool auto_part;  // the partition length is the library's to choose
   size_t partial_bytes;
+  size_t order_bytes;  // ranks, 16-byte rounded
   size_t ws_bytes;
 };
 
 Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part_blocks) {
-  if (part_blocks <= 0) part_blocks = default_partition_blocks(d, num_seqs, max_ctx);
   Plan p;
+  p.auto_part = part_blocks <= 0;
+  if (part_blocks <= 0) part_blocks = default_partition_blocks(d, num_seqs, max_ctx);
   p.part_tokens = part_blocks * kPartUnit;
   p.max_parts = max(1, (max_ctx + p.part_tokens - 1) / p.part_tokens);
   p.partial_bytes = p.max_parts <= 1 ? 0
                                      : (size_t)num_seqs * d->num_q_heads * p.max_parts *
                                            (size_t)(d->head_dim + 2) * sizeof(float);
   const int64_t ranks = (int64_t)num_seqs * p.max_parts;
-  p.ordered = num_seqs <= PA_DECODE_ORDER_MAX_SEQS && ranks * item_groups(d) > kComputeUnits;
-  p.ws_bytes = p.partial_bytes + (p.ordered ? (size_t)((ranks * 4 + 15) & ~15) : 0);
+  // an order entry holds a sequence id and a partition index in 12 bits each
+  p.ordered = num_seqs <= PA_DECODE_ORDER_MAX_SEQS && p.max_parts <= 4096 &&
+              ranks * item_groups(d) > kComputeUnits;
+  p.order_bytes = p.ordered ? (size_t)((ranks * 4 + 15) & ~15) : 0;
+  // then the partition length the order kernel chose (16 bytes)
+  p.ws_bytes = p.partial_bytes + p.order_bytes + (p.ordered ? 16 : 0);
   return p;
 }
 
@@ -1345,6 +1425,9 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.block_shift = log2_int(desc->block_size);
   a.scale_log2 = scale * kLog2e;
   a.order = plan.ordered ? (int32_t*)((char*)workspace + plan.partial_bytes) : nullptr;
+  a.part_dev = plan.ordered
+                   ? (int32_t*)((char*)workspace + plan.partial_bytes + plan.order_bytes)
+                   : nullptr;
   a.group = G;
 
   hipStream_t s = (hipStream_t)stream;
@@ -1375,8 +1458,10 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
     return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for %d kv-heads per wave", who, kpw);
   if (plan.ordered) {
     const int round = (int)max((int64_t)1, kComputeUnits / item_groups(desc));
+    PartRule rule = part_rule(desc);
+    if (!plan.auto_part) rule.auto_units = 0;
     hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a,
-                       num_seqs * plan.max_parts, round);
+                       num_seqs * plan.max_parts, round, rule);
     rc = launch_status(who);
     if (rc) return rc;
   }

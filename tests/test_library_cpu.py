@@ -83,22 +83,23 @@ def test_host_argument_checks_need_no_gpu(lib):
     assert lib.pa_decode_workspace_size(ctypes.byref(d), 4, 256) == 0
     # more work items (sequence x pair of kv-heads x partition) than the 256
     # CUs: the partials plus one int32 dispatch rank per (sequence,
-    # partition), 16-byte rounded, up to 4096 sequences
+    # partition), 16-byte rounded, and 16 bytes for the partition length the
+    # order kernel chooses, up to 4096 sequences
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 256, 8192, 1) == \
-        256 * 32 * 32 * (128 + 2) * 4 + 256 * 32 * 4
-    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4096, 256, 1) == 4096 * 4
+        256 * 32 * 32 * (128 + 2) * 4 + 256 * 32 * 4 + 16
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4096, 256, 1) == 4096 * 4 + 16
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4097, 256, 1) == 0
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 64, 256, 1) == 0  # 256 items
-    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 65, 256, 1) == 65 * 4 + 12
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 65, 256, 1) == 65 * 4 + 12 + 16
     # group size 8 at d 128 (matrix-core items of two kv-heads): 4,096-token
     # partitions once the waves (one per kv-head) fill a quarter of the 2,048
     # slots, so 64 sequences of up to 8,192 tokens take 2 partitions
     g8 = _desc(h_q=64, h_kv=8)
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(g8), 64, 8192, 0) == \
-        64 * 64 * 2 * (128 + 2) * 4 + 64 * 2 * 4
+        64 * 64 * 2 * (128 + 2) * 4 + 64 * 2 * 4 + 16
     # 32 sequences: 2,048-token partitions (4 per sequence)
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(g8), 32, 8192, 0) == \
-        32 * 64 * 4 * (128 + 2) * 4 + 32 * 4 * 4
+        32 * 64 * 4 * (128 + 2) * 4 + 32 * 4 * 4 + 16
     need = lib.pa_decode_workspace_size(ctypes.byref(d), 4, 4096)
     assert need > 0
     fake = ctypes.c_void_p(0x1000)
