@@ -128,7 +128,7 @@ __device__ __forceinline__ Parts split_parts(int n, int P, int max_parts) {
 constexpr int kPartUnit = 256;
 
 // Tokens per partition of this call: the host's, or the order kernel's
-// choice when it ran (never shorter than the host's, so never more parts).
+// choice when it ran (never shorter than the grid and workspace allow).
 __device__ __forceinline__ int part_tokens(const DecodeArgs& a) {
   return a.part_dev ? __builtin_amdgcn_readfirstlane(*a.part_dev) : a.part_tokens;
 }
@@ -685,11 +685,13 @@ __device__ __forceinline__ int dispatch_slot(int r, int round, int max_items) {
 }
 
 // PartRule: the host's partition heuristic (default_partition_blocks), which
-// estimates the mean length as half the longest; the order kernel reads
-// every length and applies it to the true mean. auto_units = 0: the caller
-// fixed the partition length.
+// estimates the mean length as half the longest. The order kernel reads
+// every length and applies it to the tokens themselves (a short sequence
+// counts its tokens, not a whole partition), between min_units and
+// auto_units. auto_units = 0: the caller fixed the partition length.
 struct PartRule {
   int auto_units;  // longest partition tried, in units of 256 tokens (0: keep the host's)
+  int min_units;   // shortest allowed: the workspace and grid hold that many partitions
   int waves;       // waves per sequence and partition
   int fill;        // waves that count as filling the chip
 };
@@ -720,21 +722,29 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
   }
   __syncthreads();
   if (t == 0) {
-    // the longest partition whose item count still fills the chip, never
-    // shorter than the host's (the workspace holds max_parts partitions of
-    // the host's length)
+    // the host's rule on the true mean length (the longest partition whose
+    // item count fills the chip), shortened further when the tokens
+    // themselves would fill less than half of it (one long sequence among
+    // short ones: each short one counts as a whole item but holds little
+    // work), no shorter than the workspace and grid allow
     int P = a.part_tokens;
     if (rule.auto_units > 0) {
       const double mean = fmax(1.0, floor((double)sum_len / a.num_seqs));
-      int units = 1;
-      for (int u = rule.auto_units; u > 1; u >>= 1) {
+      int by_items = rule.min_units, by_tokens = rule.min_units;
+      for (int u = rule.auto_units; u > rule.min_units; u >>= 1) {
         const double per_seq = ceil(mean / (u * kPartUnit));
         if ((double)a.num_seqs * rule.waves * per_seq >= rule.fill) {
-          units = u;
+          by_items = u;
           break;
         }
       }
-      P = max(P, units * kPartUnit);
+      for (int u = rule.auto_units; u > rule.min_units; u >>= 1) {
+        if (2.0 * (double)sum_len * rule.waves >= (double)rule.fill * u * kPartUnit) {
+          by_tokens = u;
+          break;
+        }
+      }
+      P = min(by_items, by_tokens) * kPartUnit;
     }
     chosen = P;
     *a.part_dev = P;
@@ -1294,6 +1304,7 @@ PartRule part_rule(const pa_desc* d) {
   const bool mf = use_mf(d);
   PartRule r;
   r.auto_units = (kpw > 1 || mf) ? 16 : 8;
+  r.min_units = 1;
   r.waves = mf ? d->num_kv_heads : item_groups(d);
   r.fill = (int)(mf && mf_waves(d) > 1 ? kResidentItems / 4 : kResidentItems / 2);
   return r;
@@ -1316,8 +1327,16 @@ int default_partition_blocks(const pa_desc* d, int32_t num_seqs, int32_t max_ctx
 // matters even when every item is resident at once: a CU's share of HBM
 // bandwidth is bounded, and longest first deals the long items out across
 // the CUs instead of stacking some on a few.
+// The dispatch order is computed when the grid has more items than CUs and
+// an order entry can hold a sequence id and a partition index (12 bits each).
+bool ordered_grid(const pa_desc* d, int32_t num_seqs, int max_parts) {
+  return num_seqs <= PA_DECODE_ORDER_MAX_SEQS && max_parts <= 4096 &&
+         (int64_t)num_seqs * max_parts * item_groups(d) > kComputeUnits;
+}
+
 struct Plan {
   int part_tokens;
+  int min_units;  // shortest partition the order kernel may choose, in 256 tokens
   int max_parts;
   bool ordered;
   bool auto_part;  // the partition length is the library's to choose
@@ -1331,14 +1350,24 @@ Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part
   p.auto_part = part_blocks <= 0;
   if (part_blocks <= 0) part_blocks = default_partition_blocks(d, num_seqs, max_ctx);
   p.part_tokens = part_blocks * kPartUnit;
+  p.min_units = part_blocks;
   p.max_parts = max(1, (max_ctx + p.part_tokens - 1) / p.part_tokens);
+  if (p.auto_part && ordered_grid(d, num_seqs, p.max_parts)) {
+    // the order kernel may cut down to a quarter of the estimate: room for
+    // that many partitions (a grid 4x the items it fills measured no slower;
+    // 16x cost 1.6% at the Qwen3-8B batch)
+    const int units = max(1, part_blocks / 4);
+    const int parts = max(1, (max_ctx + units * kPartUnit - 1) / (units * kPartUnit));
+    if (ordered_grid(d, num_seqs, parts)) {
+      p.min_units = units;
+      p.max_parts = parts;
+    }
+  }
   p.partial_bytes = p.max_parts <= 1 ? 0
                                      : (size_t)num_seqs * d->num_q_heads * p.max_parts *
                                            (size_t)(d->head_dim + 2) * sizeof(float);
   const int64_t ranks = (int64_t)num_seqs * p.max_parts;
-  // an order entry holds a sequence id and a partition index in 12 bits each
-  p.ordered = num_seqs <= PA_DECODE_ORDER_MAX_SEQS && p.max_parts <= 4096 &&
-              ranks * item_groups(d) > kComputeUnits;
+  p.ordered = ordered_grid(d, num_seqs, p.max_parts);
   p.order_bytes = p.ordered ? (size_t)((ranks * 4 + 15) & ~15) : 0;
   // then the partition length the order kernel chose (16 bytes)
   p.ws_bytes = p.partial_bytes + p.order_bytes + (p.ordered ? 16 : 0);
@@ -1459,6 +1488,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   if (plan.ordered) {
     const int round = (int)max((int64_t)1, kComputeUnits / item_groups(desc));
     PartRule rule = part_rule(desc);
+    rule.min_units = plan.min_units;
     if (!plan.auto_part) rule.auto_units = 0;
     hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, a,
                        num_seqs * plan.max_parts, round, rule);

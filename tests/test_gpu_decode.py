@@ -235,3 +235,14 @@ def test_running_max_moves_many_times(h_q, h_kv):
     out, caches, slots, before = run_decode_step(case, poison=True)
     kc_ref, vc_ref = check_store(case, caches, slots, before)
     check_decode(case, out, kc_ref, vc_ref)
+
+
+def test_skewed_batch_cut_finely():
+    """One 8,192-token sequence among 63 short ones: the order kernel counts
+    the tokens and cuts the long sequence into 256-token partitions (32
+    parts, below the host's estimate of 1,024); every row vs the oracle."""
+    lens = [8192] + [100] * 63
+    case = W.decode_case(32, 8, 128, lens, seed=80)
+    out, caches, slots, before = run_decode_step(case)
+    kc_ref, vc_ref = check_store(case, caches, slots, before)
+    check_decode(case, out, kc_ref, vc_ref)

@@ -91,15 +91,20 @@ def test_host_argument_checks_need_no_gpu(lib):
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4097, 256, 1) == 0
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 64, 256, 1) == 0  # 256 items
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 65, 256, 1) == 65 * 4 + 12 + 16
-    # group size 8 at d 128 (matrix-core items of two kv-heads): 4,096-token
-    # partitions once the waves (one per kv-head) fill a quarter of the 2,048
-    # slots, so 64 sequences of up to 8,192 tokens take 2 partitions
+    # group size 8 at d 128 (matrix-core items of two kv-heads): the host
+    # estimates 4,096-token partitions once the waves (one per kv-head) fill a
+    # quarter of the 2,048 slots; with the dispatch order the workspace holds
+    # partitions down to a quarter of that (the order kernel may cut finer),
+    # so 64 sequences of up to 8,192 tokens take up to 8 partitions
     g8 = _desc(h_q=64, h_kv=8)
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(g8), 64, 8192, 0) == \
-        64 * 64 * 2 * (128 + 2) * 4 + 64 * 2 * 4 + 16
-    # 32 sequences: 2,048-token partitions (4 per sequence)
+        64 * 64 * 8 * (128 + 2) * 4 + 64 * 8 * 4 + 16
+    # 32 sequences: 2,048-token estimate, up to 16 partitions of 512
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(g8), 32, 8192, 0) == \
-        32 * 64 * 4 * (128 + 2) * 4 + 32 * 4 * 4 + 16
+        32 * 64 * 16 * (128 + 2) * 4 + 32 * 16 * 4 + 16
+    # an explicit partition length is kept: 2 partitions of 4,096
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(g8), 64, 8192, 16) == \
+        64 * 64 * 2 * (128 + 2) * 4 + 64 * 2 * 4 + 16
     need = lib.pa_decode_workspace_size(ctypes.byref(d), 4, 4096)
     assert need > 0
     fake = ctypes.c_void_p(0x1000)
