@@ -88,8 +88,8 @@ int pa_store_kv(const void* k, int64_t k_row_stride, const void* v, int64_t v_ro
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for
  * this batch geometry: split-K partial results when a sequence can span
  * more than one partition, and a longest-first dispatch order (with the
- * partition length chosen on the device from the actual lengths, never
- * shorter than the host's estimate) when the grid has more work items than
+ * partition length chosen on the device from the actual lengths, down to a
+ * quarter of the host's estimate) when the grid has more work items than
  * the GPU has compute units (at most 4096 sequences). 0 when neither
  * applies, and on invalid arguments. The result depends only on the
  * arguments.
@@ -135,8 +135,9 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * pa_decode_partitioned -- pa_decode with an explicit split-K partition of
  * partition_blocks * 256 tokens per work item, whatever block_size is (whole
  * blocks at block_size 256; 0 = the library's choice, which is what pa_decode
- * uses: estimated on the host from max_context_len, and lengthened on the
- * device from the actual lengths when the dispatch order is computed). The
+ * uses: estimated on the host from max_context_len, and chosen on the
+ * device from the actual lengths, down to a quarter of that estimate, when
+ * the dispatch order is computed). The
  * result is the same attention for any partition size up to rounding.
  * Workspace: pa_decode_workspace_size_ex.
  */
