@@ -118,8 +118,12 @@ size_t pa_decode_workspace_size(const pa_desc* desc, int32_t num_seqs, int32_t m
  *                 and are never read.
  *   context_lens  device, int32 [num_seqs]; 0 <= n <= max_context_len and
  *                 ceil(n/B) <= max_blocks_per_seq.
- *   max_context_len  host upper bound of context_lens (sizes the grid).
- *   scale         softmax scale, e.g. 1/sqrt(d).
+ *   max_context_len  host upper bound of context_lens (sizes the grid);
+ *                 at most 2^30.
+ *   scale         softmax scale, e.g. 1/sqrt(d); must be positive and finite
+ *                 (PA_ERR_INVALID_ARG otherwise): the kernels take the
+ *                 maximum of the unscaled scores and scale it, which is the
+ *                 maximum of the scaled scores only for a positive scale.
  *   out           device, bf16 [num_seqs, H_q, d]; must not alias inputs.
  *   workspace     device, >= pa_decode_workspace_size(...) bytes, 16-byte
  *                 aligned; may be NULL when that size is 0. Contents on entry
@@ -137,9 +141,11 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * blocks at block_size 256; 0 = the library's choice, which is what pa_decode
  * uses: estimated on the host from max_context_len, and chosen on the
  * device from the actual lengths, down to a quarter of that estimate, when
- * the dispatch order is computed). The
- * result is the same attention for any partition size up to rounding.
- * Workspace: pa_decode_workspace_size_ex.
+ * the dispatch order is computed). A partition longer than
+ * ceil(max_context_len / 256) units is cut to that length (it already holds
+ * every sequence whole). The result is the same attention for any partition
+ * size up to rounding. Workspace: pa_decode_workspace_size_ex (the same
+ * cut applies).
  */
 int pa_decode_partitioned(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -165,7 +171,7 @@ size_t pa_decode_workspace_size_ex(const pa_desc* desc, int32_t num_seqs,
  * with n == 0 get zeros and store nothing.
  *
  *   q, block_tables, context_lens, max_context_len, scale, out, workspace:
- *                 as pa_decode (same workspace size).
+ *                 as pa_decode (same workspace size and preconditions).
  *   k_new, v_new  device, bf16 [num_seqs, H_kv, d], row strides in elements
  *                 (multiples of 8, >= H_kv*d), 16-byte aligned.
  *   k_cache, v_cache  device, written (one row per sequence) and read.
@@ -197,6 +203,8 @@ int pa_decode_step(const void* q, const void* k_new, int64_t k_row_stride, const
  *   max_seqlen_q, max_seqlen_k  host upper bounds of q_len and k_len.
  *   block_tables  device, int32 [num_seqs, max_blocks_per_seq]; entries for
  *                 blocks 0 .. ceil(k_len/B)-1 in [0, N).
+ *   scale         as pa_decode: positive and finite (PA_ERR_INVALID_ARG
+ *                 otherwise).
  *   out           device, bf16 [total_q, H_q, d].
  */
 int pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,

@@ -231,11 +231,14 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.pa_decode_partitioned(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                     block_tables.data_ptr(), max_blocks, context_lens.data_ptr(),
-                                     batch, int(max_context_len), float(scale), out.data_ptr(),
-                                     ws_ptr, ws_bytes, int(partition_blocks), ctypes.byref(desc),
-                                     _stream(q)))
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+            max_blocks, context_lens.data_ptr(), batch, int(max_context_len), float(scale),
+            out.data_ptr(), ws_ptr, ws_bytes)
+    if partition_blocks:
+        _check(lib.pa_decode_partitioned(*args, int(partition_blocks), ctypes.byref(desc),
+                                         _stream(q)))
+    else:  # the library's partition choice: the plain entry point
+        _check(lib.pa_decode(*args, ctypes.byref(desc), _stream(q)))
 
 
 def pa_decode_step(q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens,

@@ -26,7 +26,7 @@
 //   * loads: 16 bytes per lane, nontemporal (K/V are read once); d/8 lanes
 //     cover one kv-head vector and KPW adjacent kv-heads make a 512-byte
 //     contiguous piece of a token row. A chunk is eight loads of K and
-//     eight of V (four with 8 q-heads per kv-head), and the next chunk's
+//     eight of V, and the next chunk's
 //     loads are issued before the current chunk is multiplied (two register
 //     buffers; block-table entries are read two chunks ahead).
 //   * q.k: v_dot2_f32_bf16 on the raw bf16 pairs (exact products, fp32 sum),
@@ -37,8 +37,9 @@
 //     once at the end.
 //   * P.V: weights rounded to bf16 pairs, v_dot2_f32_bf16 on paired V rows,
 //     fp32 accumulation; the sum adds the same rounded weights.
-//   * 8 or 16 q-heads per kv-head at d = 128: the vector work per byte grows
-//     with the group and would bound the kernel, so both products run on
+//   * 8 or more q-heads per kv-head (and group sizes that are not powers of
+//     two): the vector work per byte grows with the group and would bound
+//     the kernel, so both products run on
 //     the matrix cores instead (v_mfma_f32_16x16x32_bf16, the q-heads as
 //     the 16 columns), with each chunk's K rows and V^T staged through a
 //     per-wave LDS region (compute_chunk_mf). Loads, pipeline and dispatch
@@ -126,6 +127,9 @@ __device__ __forceinline__ Parts split_parts(int n, int P, int max_parts) {
 
 // Partition lengths are counted in units of 256 tokens, whatever the block size.
 constexpr int kPartUnit = 256;
+// Longest partition (units): 2^30 tokens, the longest context accepted.
+constexpr int kMaxPartUnits = 1 << 22;
+constexpr int32_t kMaxContext = kMaxPartUnits * kPartUnit;
 
 // Tokens per partition of this call: the host's, or the order kernel's
 // choice when it ran (never shorter than the grid and workspace allow).
@@ -148,42 +152,18 @@ __device__ __forceinline__ int64_t token_offset(const DecodeArgs& a, const int32
   return block_offset(a, bt[pos >> a.block_shift], pos, row_bytes);
 }
 
-#ifndef PA_DECODE_UNROLL
-#define PA_DECODE_UNROLL 8
-#endif
-
-// Load instructions per chunk. With 8 q-heads per kv-head the scores and
-// accumulators of 8 loads no longer fit the register file next to two load
-// buffers, so that group size takes chunks of 4.
-constexpr int unroll_for(int G) { return G >= 8 ? 4 : PA_DECODE_UNROLL; }
-#ifndef PA_DECODE_NT
-#define PA_DECODE_NT 1
-#endif
-#ifndef PA_DECODE_WAVES
-#define PA_DECODE_WAVES 2
-#endif
+// Load instructions per chunk on the vector path (group sizes 1, 2, 4).
+constexpr int kVecUnroll = 8;
+// Waves per SIMD the split kernel is compiled for (its register budget).
+constexpr int kSplitWavesPerSimd = 2;
 
 // K/V rows are read exactly once per call: nontemporal loads keep them from
 // displacing reusable lines (tables, q) in the caches.
 __device__ __forceinline__ uint4 load16(const char* p) {
-#if PA_DECODE_NT
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(r.x, r.y, r.z, r.w);
-#else
-  return *reinterpret_cast<const uint4*>(p);
-#endif
 }
-
-#ifndef PA_DECODE_PV_BF16
-#define PA_DECODE_PV_BF16 1
-#endif
-#ifndef PA_DECODE_PIPE
-#define PA_DECODE_PIPE 1
-#endif
-#ifndef PA_DECODE_DRAIN
-#define PA_DECODE_DRAIN 1
-#endif
 
 // Before a chunk's loads are issued (U loads each of K and V), optionally
 // wait until the previous chunk's loads have all arrived (s_waitcnt
@@ -197,12 +177,10 @@ __device__ __forceinline__ uint4 load16(const char* p) {
 // per SIMD), so the host picks the kernel. Chunks of 4 loads never wait.
 template <int U, bool DRAIN>
 __device__ __forceinline__ void drain_loads() {
-#if PA_DECODE_DRAIN
   if constexpr (DRAIN && U == 8) {
     __builtin_amdgcn_sched_barrier(0);  // not hoisted into the multiply before it
     __builtin_amdgcn_s_waitcnt(0x0F70);
   }
-#endif
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
@@ -262,10 +240,6 @@ __device__ __forceinline__ void issue_chunk_groups(const char* kc, const char* v
 #pragma unroll
   for (int u = 0; u < U; ++u) vr[u] = load16(vc + off[u] + lane_off);
 }
-
-#ifndef PA_DECODE_TRANSPOSE
-#define PA_DECODE_TRANSPOSE 1
-#endif
 
 // DPP lane maps inside a 16-lane row (checked on gfx950): lane i reads lane
 // i^1, i^2, i^7 (mirror inside each 8-lane half) or i^8 (rotate by 8), or
@@ -381,7 +355,7 @@ template <class S, int D, int G, int U, bool TAIL>
 __device__ __forceinline__ void compute_chunk_v(SplitState<D, G>& st, float scale_log2, int row,
                                               int nvalid, const uint4 (&kr)[U],
                                               const uint4 (&vr)[U]) {
-  if constexpr (PA_DECODE_TRANSPOSE && S::LPT == 16 && (U == 4 || U == 8)) {
+  if constexpr (S::LPT == 16 && (U == 4 || U == 8)) {
     compute_chunk_t<S, D, G, U, TAIL>(st, scale_log2, row, nvalid, kr, vr);
     return;
   }
@@ -413,10 +387,12 @@ __device__ __forceinline__ void compute_chunk_v(SplitState<D, G>& st, float scal
     st.m[h] = mnew;
     negm[h] = -msafe;
   }
-  if constexpr (PA_DECODE_PV_BF16 && U % 2 == 0) {
+  if constexpr (U % 2 == 0) {
   // P.V on token pairs with v_dot2_f32_bf16: (V[t][e], V[t+1][e]) packed by
   // v_perm, weights rounded to bf16 as the MFMA prefill does. The sum l adds
   // the same rounded weights, so the output stays an exact weighted mean.
+  // (A single token -- the fused step's newest one at d = 64 -- takes the
+  // fp32 form below.)
 #pragma unroll
   for (int u = 0; u < U; u += 2) {
     uint32_t ppair[G];
@@ -649,14 +625,12 @@ __device__ __forceinline__ void compute_chunk(St& st, char* lds, float scale_log
 // full partitions in the top one; empty sequences, which only write zeros,
 // last). One workgroup ranks them before the split kernel runs (a histogram
 // of the buckets, then each item takes the next rank of its bucket) and
-// writes order[slot] = (P / 256) << 24 | part << 12 | sequence (P: the
-// partition length it chose), -1 past the last item (slot:
-// the rank laid out by dispatch_slot); a split wave reads its one entry. (Each wave ranking
+// writes order[slot] = part << 12 | sequence, -1 past the last item (slot:
+// the rank laid out by dispatch_slot), and the partition length it chose
+// to the workspace; a split wave reads its one entry. (Each wave ranking
 // the items itself from the lengths cost it 8-24 us: every wave read the
 // same lengths.)
-#ifndef PA_DECODE_ORDER_MAX_SEQS
-#define PA_DECODE_ORDER_MAX_SEQS 4096  // sequence ids must fit 12 bits
-#endif
+constexpr int kOrderMaxSeqs = 4096;  // sequence ids must fit 12 bits
 constexpr int kOrderBuckets = 32;
 constexpr int kOrderThreads = 1024;
 
@@ -664,9 +638,6 @@ __device__ __forceinline__ int len_bucket(int len, int part_tokens) {
   return 1 + (int)(((int64_t)(len - 1) * kOrderBuckets) / part_tokens);  // 1..32
 }
 
-#ifndef PA_DECODE_SNAKE
-#define PA_DECODE_SNAKE 1
-#endif
 
 // Where rank r goes in the dispatch order. Workgroups are dealt to the CUs
 // in launch order, a round of `round` items (one per CU) at a time; in
@@ -674,14 +645,10 @@ __device__ __forceinline__ int len_bucket(int len, int part_tokens) {
 // first CU would get the longest item of every round. Odd rounds are
 // reversed, so each CU gets a long and a short item in turn.
 __device__ __forceinline__ int dispatch_slot(int r, int round, int max_items) {
-#if PA_DECODE_SNAKE
   const int k = r / round;
   const int start = k * round;
   const int len = min(round, max_items - start);
   return (k & 1) ? start + len - 1 - (r - start) : r;
-#else
-  return r;
-#endif
 }
 
 // PartRule: the host's partition heuristic (default_partition_blocks), which
@@ -702,7 +669,7 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
   __shared__ int next[NB];  // counts, then the next free rank of each bucket
   __shared__ int total;
   // each length read once from memory (the host orders at most this many)
-  __shared__ int lens[PA_DECODE_ORDER_MAX_SEQS > 0 ? PA_DECODE_ORDER_MAX_SEQS : 1];
+  __shared__ int lens[kOrderMaxSeqs];
   __shared__ unsigned long long sum_len;
   __shared__ int chosen;
   const int t = threadIdx.x;
@@ -751,7 +718,6 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
   }
   __syncthreads();
   const int P = chosen;
-  const int tag = (P / kPartUnit) << 24;  // the partition length travels with every entry
   // a sequence's items: `bulk` full partitions in bucket kb (the top one),
   // then its last part in bucket kl (an empty sequence: one item, in bucket 0)
   auto items = [&](int s, int& bulk, int& kb, int& kl) {
@@ -795,9 +761,9 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
     if (bulk) {
       const int pos = atomicAdd(&next[kb], bulk);
       for (int j = 0; j < bulk; ++j)
-        order[dispatch_slot(pos + j, round, max_items)] = tag | (j << 12) | s;
+        order[dispatch_slot(pos + j, round, max_items)] = (j << 12) | s;
     }
-    order[dispatch_slot(atomicAdd(&next[kl], 1), round, max_items)] = tag | (bulk << 12) | s;
+    order[dispatch_slot(atomicAdd(&next[kl], 1), round, max_items)] = (bulk << 12) | s;
   }
   for (int r = total + t; r < max_items; r += kOrderThreads)
     order[dispatch_slot(r, round, max_items)] = -1;
@@ -806,21 +772,18 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
 // A work item is (sequence, group of KPW adjacent kv-heads, partition).
 // SMALL: blocks hold fewer tokens than a chunk, so each load group looks up
 // its own block; otherwise a chunk lies inside one block.
-// Vector path: VS waves per workgroup share a kv-head, each with G of its
-// q-heads (VS = 2 at 16 q-heads per kv-head: a wave holds at most 8); they
-// read the same K/V rows on the same CU, so the second read is served by its
-// caches.
+// Vector path (G = 1, 2, 4): one wave per workgroup (VS = 1).
 // MF: the matrix-core variant (KPW = 1, G <= 16; G = 0 takes the group
 // size from the arguments); with VS > 1 its waves take VS adjacent kv-heads,
 // one each.
 template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1, bool MF = false>
-__global__ __launch_bounds__(kWave * VS) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES)))
+__global__ __launch_bounds__(kWave * VS) __attribute__((amdgpu_waves_per_eu(kSplitWavesPerSimd)))
 void decode_split_kernel(DecodeArgs a) {
   static_assert(!MF || (KPW == 1 && G <= 16 && VS <= 4), "matrix-core geometry");
   static_assert(MF || G > 0, "the vector path is built per group size");
   const int Gn = G ? G : a.group;  // q-heads per kv-head
   constexpr bool kPair = MF && VS > 1;  // one kv-head per wave, VS per workgroup
-  constexpr int U = MF ? D / 16 : unroll_for(G);  // matrix cores: chunks of 32 tokens
+  constexpr int U = MF ? D / 16 : kVecUnroll;  // matrix cores: chunks of 32 tokens
   using S = typename std::conditional<MF, MfState<D>, SplitState<D, (G ? G : 1)>>::type;
   using L = Lanes<D, KPW>;
   constexpr int LPT = L::LPT;
@@ -841,7 +804,7 @@ void decode_split_kernel(DecodeArgs a) {
     if (v < 0) return;
     b = __builtin_amdgcn_readfirstlane(v & 4095);
     part = __builtin_amdgcn_readfirstlane((v >> 12) & 4095);
-    P = __builtin_amdgcn_readfirstlane((v >> 24) * kPartUnit);
+    P = part_tokens(a);  // the length the order kernel chose
   } else {
     // highest partition first
     const int idx = blockIdx.x / n_groups;
@@ -939,7 +902,6 @@ void decode_split_kernel(DecodeArgs a) {
       issue_chunk_groups<U>(kc, vc, off, lane_off, kr, vr);
     }
   };
-#if PA_DECODE_PIPE
   // Software pipeline over two register buffers: chunk i+1's loads are in
   // flight while chunk i is multiplied, and the table entry of chunk i+2 is
   // read before chunk i+1's loads are issued, so it has arrived by the time
@@ -947,17 +909,13 @@ void decode_split_kernel(DecodeArgs a) {
   // latency in front of every chunk; after a drain the compiler makes table
   // reads vector loads, which complete in order behind the chunk's loads).
   // The loop body has no branches. The last one or two chunks are finished
-  // after the loop, so no chunk is loaded twice; with 8 q-heads on the
-  // vector path that epilogue no longer fits the register file, and the loop
-  // instead runs to the end with the prefetch clamped (the last chunk is
-  // then loaded twice).
+  // after the loop, so no chunk is loaded twice.
   if (nfull > 0) {
-    constexpr bool kEpilogue = MF || G < 8;
     uint4 ka[U], va[U], kb[U], vb[U];
     issue(lookup(0), ka, va);
     Lookup next = lookup(1);
     int i = 0;
-    for (; kEpilogue ? i + 2 < nfull : i + 2 <= nfull; i += 2) {
+    for (; i + 2 < nfull; i += 2) {
       drain_loads<U, DRAIN>();
       const Lookup after = lookup(i + 2);
       issue(next, kb, vb);  // chunk i+1
@@ -969,7 +927,7 @@ void decode_split_kernel(DecodeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, kb, vb);
     }
-    if (kEpilogue && i + 1 < nfull) {
+    if (i + 1 < nfull) {
       drain_loads<U, DRAIN>();
       issue(next, kb, vb);  // chunk i+1
       __builtin_amdgcn_sched_barrier(0);
@@ -979,13 +937,6 @@ void decode_split_kernel(DecodeArgs a) {
       compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, ka, va);
     }
   }
-#else
-  for (int i = 0; i < nfull; ++i) {
-    uint4 kr[U], vr[U];
-    issue(lookup(i), kr, vr);
-    compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, kr, vr);
-  }
-#endif
   const int c = start + nfull * CHUNK;
   if (c < cend) {
     // tail: every lane finds its own token's row (clamped to the last valid
@@ -1104,10 +1055,7 @@ void decode_split_kernel(DecodeArgs a) {
 // merge of up to kReduceParts partitions waits for memory once after the
 // length (against two passes over the partitions: 32 x 16,384 tokens
 // 336 -> 327 us per call, Qwen3-0.6B batch 87.6 -> 84.4 us).
-#ifndef PA_DECODE_REDUCE_WAVES
-#define PA_DECODE_REDUCE_WAVES 1
-#endif
-constexpr int kReduceWaves = PA_DECODE_REDUCE_WAVES;
+constexpr int kReduceWaves = 1;
 constexpr int kReduceParts = 8;
 
 template <int D>
@@ -1174,10 +1122,6 @@ SplitFn pick_split(int G) {
     case 1: return decode_split_kernel<D, 1, KPW, FUSED, SMALL, kD>;
     case 2: return decode_split_kernel<D, 2, KPW, FUSED, SMALL, kD>;
     case 4: return decode_split_kernel<D, 4, KPW, FUSED, SMALL, kD>;
-    case 8: return decode_split_kernel<D, 8, KPW, FUSED, SMALL, false>;
-    case 16:
-      if constexpr (KPW == 1) return decode_split_kernel<D, 8, 1, FUSED, SMALL, false, 2>;
-      return nullptr;
   }
   return nullptr;
 }
@@ -1223,54 +1167,33 @@ SplitFn pick_split(int G, bool fused, bool small, bool drain) {
   return fused ? pick_split<D, KPW, true>(G, small, drain) : pick_split<D, KPW, false>(G, small, drain);
 }
 
-#ifndef PA_DECODE_SEGMENT
-#define PA_DECODE_SEGMENT 512
-#endif
+constexpr int kSegmentBytes = 512;
 
-// kv-heads per wave: as many adjacent heads as make a PA_DECODE_SEGMENT-byte
+// kv-heads per wave: as many adjacent heads as make a kSegmentBytes-byte
 // contiguous piece of each token row (on MI355X 512-byte pieces stream about
 // 7% faster than 256-byte ones), when the head count allows it; else one.
-// With 8 q-heads per kv-head the wave's arithmetic per byte is highest and
-// its chunks are shortest; there one kv-head per wave measures faster (and
-// the matrix-core variant takes one kv-head per wave).
-// Waves per kv-head: a vector-path wave holds at most 8 q-heads, so 16
-// q-heads per kv-head take two waves of one workgroup at d = 64.
-#ifndef PA_DECODE_MF_MIN_G
-#define PA_DECODE_MF_MIN_G 8
-#endif
-#ifndef PA_DECODE_MF64_MIN_G
-#define PA_DECODE_MF64_MIN_G 8
-#endif
-// Group sizes from PA_DECODE_MF_MIN_G (d = 128) or PA_DECODE_MF64_MIN_G
-// (d = 64) up, and those that are not powers of two, run on the matrix cores.
-bool mf_group(int head_dim, int G) {
-  const int min_g = head_dim == 128 ? PA_DECODE_MF_MIN_G : PA_DECODE_MF64_MIN_G;
-  return G >= min_g || (G & (G - 1)) != 0;
-}
+// The matrix-core variant takes one kv-head per wave.
+// Group sizes from 8 up, and those that are not powers of two, run on the
+// matrix cores (at both head dims); 1, 2 and 4 on the vector path.
+bool mf_group(int /*head_dim*/, int G) { return G >= 8 || (G & (G - 1)) != 0; }
 bool use_mf(const pa_desc* d) { return mf_group(d->head_dim, d->num_q_heads / d->num_kv_heads); }
-#ifndef PA_DECODE_MF_GROUP
-#define PA_DECODE_MF_GROUP 2
-#endif
-// Matrix-core items: PA_DECODE_MF_GROUP adjacent kv-heads (fewer when the
-// head count does not divide), one wave each, in one workgroup.
+// Matrix-core items: two adjacent kv-heads (one when the head count is odd),
+// one wave each, in one workgroup.
 int mf_waves(const pa_desc* d) {
   if (!use_mf(d)) return 0;
-  int w = PA_DECODE_MF_GROUP;
+  int w = 2;
   while (w > 1 && d->num_kv_heads % w) w >>= 1;
   return w;
 }
-int kv_split(const pa_desc* d) {
-  if (use_mf(d)) return mf_waves(d);
-  return d->num_q_heads / d->num_kv_heads > 8 ? 2 : 1;
-}
+// Waves per split-kernel workgroup.
+int kv_split(const pa_desc* d) { return use_mf(d) ? mf_waves(d) : 1; }
 
 // Work-item groups per sequence: kv-heads over kv-heads per wave.
 int item_groups(const pa_desc* d);
 
 int kv_heads_per_wave(int head_dim, int num_q_heads, int num_kv_heads) {
-  if (num_q_heads / num_kv_heads >= 8) return 1;
   if (mf_group(head_dim, num_q_heads / num_kv_heads)) return 1;
-  const int want = PA_DECODE_SEGMENT / (2 * head_dim);
+  const int want = kSegmentBytes / (2 * head_dim);
   return (want > 1 && num_kv_heads % want == 0) ? want : 1;
 }
 
@@ -1330,7 +1253,7 @@ int default_partition_blocks(const pa_desc* d, int32_t num_seqs, int32_t max_ctx
 // The dispatch order is computed when the grid has more items than CUs and
 // an order entry can hold a sequence id and a partition index (12 bits each).
 bool ordered_grid(const pa_desc* d, int32_t num_seqs, int max_parts) {
-  return num_seqs <= PA_DECODE_ORDER_MAX_SEQS && max_parts <= 4096 &&
+  return num_seqs <= kOrderMaxSeqs && max_parts <= 4096 &&
          (int64_t)num_seqs * max_parts * item_groups(d) > kComputeUnits;
 }
 
@@ -1349,6 +1272,11 @@ Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part
   Plan p;
   p.auto_part = part_blocks <= 0;
   if (part_blocks <= 0) part_blocks = default_partition_blocks(d, num_seqs, max_ctx);
+  // A partition at least as long as the longest context holds every
+  // sequence whole, whatever its length: longer requests are cut to that.
+  const int64_t whole = max((int64_t)1, min(((int64_t)max_ctx + kPartUnit - 1) / kPartUnit,
+                                            (int64_t)kMaxPartUnits));
+  part_blocks = (int)min((int64_t)part_blocks, whole);
   p.part_tokens = part_blocks * kPartUnit;
   p.min_units = part_blocks;
   p.max_parts = max(1, (max_ctx + p.part_tokens - 1) / p.part_tokens);
@@ -1387,6 +1315,14 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   if (rc) return rc;
   if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || partition_blocks < 0)
     return fail(PA_ERR_INVALID_ARG, "%s: negative size", who);
+  if (max_context_len > kMaxContext)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_context_len %d above %d", who, max_context_len,
+                kMaxContext);
+  // the kernels take the maximum of the raw scores and scale it afterwards,
+  // which equals the maximum of the scaled scores only for a positive scale
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PA_ERR_INVALID_ARG, "%s: scale %g must be positive and finite", who,
+                (double)scale);
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !(context_lens || cu_k) || !out)
     return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", who);
@@ -1461,7 +1397,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
 
   hipStream_t s = (hipStream_t)stream;
   const bool mf = use_mf(desc);
-  const int chunk = mf ? 32 : (kWave / (D / 8 * kpw)) * unroll_for(min(G, 8));  // tokens per chunk
+  const int chunk = mf ? 32 : (kWave / (D / 8 * kpw)) * kVecUnroll;  // tokens per chunk
   const bool small = desc->block_size < chunk;
   const bool fused = nt != nullptr;
   // the wave slots are full (2 per SIMD): one chunk of loads in flight per wave

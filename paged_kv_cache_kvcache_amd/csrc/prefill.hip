@@ -43,18 +43,9 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 8
-#endif
-#ifndef PA_PREFILL_NT
-#define PA_PREFILL_NT 2
-#endif
-#ifndef PA_PREFILL_LAZY
-#define PA_PREFILL_LAZY 1
-#endif
-constexpr int kWaves = PA_PREFILL_WAVES;  // waves per workgroup
+constexpr int kWaves = 8;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
-constexpr int kNT = PA_PREFILL_NT;        // 16-column tiles per wave
+constexpr int kNT = 2;     // 16-column tiles per wave
 constexpr int kTiles = kNT * kWaves;      // 16-column tiles per workgroup
 constexpr int kCols = 16 * kTiles;        // (position, q-head) columns per workgroup
 // Lazy rescaling: a column's reference max moves only when a score exceeds
@@ -216,22 +207,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
   const int H_kv = a.num_kv_heads;
   const int H_q = H_kv * G;
-#ifndef PA_PREFILL_ORDER
-#define PA_PREFILL_ORDER 1
-#endif
   int idx = blockIdx.x;
   const int g = idx % H_kv;
   idx /= H_kv;
-#if PA_PREFILL_ORDER == 1
   // A sequence's position blocks are consecutive (last positions first) and
   // kv-head is fastest, so the blocks of one (sequence, kv-head), which read
   // the same K/V, run together on one XCD and share its L2.
   const int r = idx % a.max_rblocks;  // position block counted from the end
   const int b = idx / a.max_rblocks;
-#else
-  const int b = idx % a.num_seqs;
-  const int r = idx / a.num_seqs;  // position block counted from the end
-#endif
 
   const int q0 = a.cu_q[b];
   const int q_len = a.cu_q[b + 1] - q0;
@@ -330,12 +313,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
       mx = fmaxf(mx, xor_lane(mx, 16));
       mx = fmaxf(mx, xor_lane(mx, 32));
       mx *= a.scale_log2;
-#if PA_PREFILL_LAZY
       // all lanes of a column see the same mx and m, so they agree on it
       if (mx > m[j] + kLazyLog2) {
-#else
-      {
-#endif
         const float mnew = fmaxf(m[j], mx);
         const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);  // 0 on the first step
         m[j] = mnew;
@@ -451,6 +430,11 @@ int launch_prefill(const char* who, const void* q, const void* k_cache, const vo
   if (rc) return rc;
   if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || max_blocks_per_seq < 0)
     return fail(PA_ERR_INVALID_ARG, "%s: negative size", who);
+  // the kernel takes the maximum of the raw scores and scales it afterwards,
+  // which equals the maximum of the scaled scores only for a positive scale
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PA_ERR_INVALID_ARG, "%s: scale %g must be positive and finite", who,
+                (double)scale);
   if (num_seqs == 0 || max_seqlen_q == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_tables || !out)
     return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", who);

@@ -180,3 +180,46 @@ def test_debug_switch_needs_no_gpu(lib):
         assert lib.pa_set_debug(0) == 0
     finally:
         lib.pa_set_debug(prev)
+
+
+def test_scale_must_be_positive_and_finite(lib):
+    """The kernels scale the maximum of the raw scores, which is the maximum
+    of the scaled scores only for scale > 0: every attention entry point
+    rejects other scales on the host, before touching any pointer."""
+    d = _desc()
+    fake = ctypes.c_void_p(0x1000)
+    for bad in (0.0, -0.125, float("nan"), float("inf"), -float("inf")):
+        assert lib.pa_decode(fake, fake, fake, fake, 16, fake, 4, 4096, bad, fake, None, 0,
+                             ctypes.byref(d), None) == B.PA_ERR_INVALID_ARG
+        assert b"scale" in lib.pa_last_error()
+        assert lib.pa_decode_partitioned(fake, fake, fake, fake, 16, fake, 4, 4096, bad, fake,
+                                         None, 0, 2, ctypes.byref(d), None) == B.PA_ERR_INVALID_ARG
+        assert lib.pa_decode_step(fake, fake, 1024, fake, 1024, fake, fake, fake, fake, 16, fake,
+                                  4, 4096, bad, fake, None, 0, ctypes.byref(d),
+                                  None) == B.PA_ERR_INVALID_ARG
+        assert lib.pa_prefill_varlen(fake, fake, fake, fake, fake, 4, 100, 4096, fake, 16, bad,
+                                     fake, ctypes.byref(d), None) == B.PA_ERR_INVALID_ARG
+        assert b"scale" in lib.pa_last_error()
+        assert lib.pa_mixed_varlen(fake, fake, fake, fake, fake, 4, 2, 100, 4096, fake, 16, bad,
+                                   fake, None, 0, ctypes.byref(d), None) == B.PA_ERR_INVALID_ARG
+    # a positive scale passes that check (and then fails on the missing workspace)
+    assert lib.pa_decode(fake, fake, fake, fake, 16, fake, 4, 4096, 0.125, fake, None, 0,
+                         ctypes.byref(d), None) == B.PA_ERR_WORKSPACE
+
+
+def test_long_partitions_are_cut_to_the_longest_context(lib):
+    """An explicit partition longer than ceil(max_context_len / 256) units
+    holds every sequence whole: the workspace equals that of the cut length
+    (no partials; the dispatch order, if any, has one entry per sequence),
+    however large the request, and a context above 2^30 is refused."""
+    d = _desc()
+    for pb in (32, 127, 128, 200, 255, 256, 4096, 2 ** 31 - 1):
+        for seqs, ctx in ((4, 8192), (65, 8192), (256, 16384)):
+            whole = -(-ctx // 256)
+            assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), seqs, ctx, pb) == \
+                lib.pa_decode_workspace_size_ex(ctypes.byref(d), seqs, ctx, min(pb, whole))
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 65, 8192, 200) == 65 * 4 + 12 + 16
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.pa_decode(fake, fake, fake, fake, 2 ** 22 + 1, fake, 4, 2 ** 30 + 1, 0.125, fake,
+                         None, 0, ctypes.byref(_desc(bsz=1024)), None) == B.PA_ERR_INVALID_ARG
+    assert b"max_context_len" in lib.pa_last_error()
