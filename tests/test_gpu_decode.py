@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_helpers import (assert_close, dev_bf16, dev_i32, host_bits, host_f64, poison_unused)
+from gpu_helpers import (assert_close, check_whole_output, dev_bf16, dev_i32, host_bits, host_f64,
+                         poison_unused)
 from paged_kv_cache_kvcache_amd import binding as B
 from paged_kv_cache_kvcache_amd import workloads as W
 
@@ -90,24 +91,15 @@ def test_store_and_decode_full_oracle(name):
     check_decode(case, out, kc_ref, vc_ref)
 
 
-def _sample_rows(ctx, k, seed):
-    order = np.argsort(ctx)
-    rng = np.random.default_rng(seed)
-    pick = {int(order[0]), int(order[-1])}
-    pick.update(int(x) for x in rng.choice(len(ctx), size=k, replace=False))
-    return sorted(pick)
-
-
 @pytest.mark.parametrize("name", ["qwen3-8b", "long", "gqa8", "gqa16"])
-def test_store_and_decode_full_size_sampled(name):
-    """Full-size workloads in the benchmark's launch configuration; the store
-    is compared in full, decode on sampled sequences (longest and shortest
-    included)."""
+def test_store_and_decode_full_size(name):
+    """Full-size workloads in the benchmark's launch configuration: the store
+    is compared with the oracle's over both whole caches, and every output
+    row with the oracle's decode (computed in a separate process)."""
     case = W.make_case(name)
     out, caches, slots, before = run_decode_step(case)
-    kc_ref, vc_ref = check_store(case, caches, slots, before)
-    rows = _sample_rows(case.context_lens, 3 if name == "long" else 6, 5)
-    check_decode(case, out, kc_ref, vc_ref, rows=rows)
+    check_store(case, caches, slots, before)
+    check_whole_output("decode", name, out)
 
 
 def test_ctx1_returns_value_bit_exact():
@@ -201,8 +193,7 @@ def test_large_batch_of_short_sequences(batch, h_q, h_kv, d):
     ranked by the order kernel (sequence ids fill its 12 bits at 4,096), one
     more keeps the plain dispatch order (highest partition first), on the
     vector path and (16 q / 2 kv heads) the matrix cores. Lengths
-    1..600 with a few padding rows; sampled rows and every padding row vs the
-    oracle."""
+    1..600 with a few padding rows; every row vs the oracle."""
     rng = np.random.default_rng(77 + batch)
     lens = rng.integers(1, 600 + 1, size=batch)
     pad = [3, 700, batch - 1]
@@ -210,9 +201,7 @@ def test_large_batch_of_short_sequences(batch, h_q, h_kv, d):
     case = W.decode_case(h_q, h_kv, d, lens, seed=78)
     out, caches, slots, before = run_decode_step(case)
     kc_ref, vc_ref = check_store(case, caches, slots, before)
-    rows = sorted(set(rng.choice(len(lens), 40, replace=False).tolist()) | set(pad) |
-                  {batch - 2, 4095 if batch > 4095 else 0})
-    check_decode(case, out, kc_ref, vc_ref, rows=rows)
+    check_decode(case, out, kc_ref, vc_ref)
     assert np.all(out[pad] == 0)
 
 
@@ -244,5 +233,20 @@ def test_skewed_batch_cut_finely():
     lens = [8192] + [100] * 63
     case = W.decode_case(32, 8, 128, lens, seed=80)
     out, caches, slots, before = run_decode_step(case)
+    kc_ref, vc_ref = check_store(case, caches, slots, before)
+    check_decode(case, out, kc_ref, vc_ref)
+
+
+@pytest.mark.parametrize("partition_blocks", [64, 128, 200])
+def test_explicit_long_partitions_on_the_ordered_grid(partition_blocks):
+    """70 sequences (more work items than CUs: the dispatch order is
+    computed) with explicit partitions of 64, 128 and 200 units of 256
+    tokens; lengths up to 9,000, so the longer requests are cut to the
+    longest context and every sequence is one partition. Every row vs the
+    oracle."""
+    rng = np.random.default_rng(82)
+    lens = rng.integers(1, 9000 + 1, size=70)
+    case = W.decode_case(32, 8, 128, lens, seed=83)
+    out, caches, slots, before = run_decode_step(case, partition_blocks=partition_blocks)
     kc_ref, vc_ref = check_store(case, caches, slots, before)
     check_decode(case, out, kc_ref, vc_ref)

@@ -51,9 +51,19 @@ def test_cu_seqlens_example_from_pages():
 
 
 def test_block_boundary_example_from_pages():
+    """The page's fact (a 256-token sequence fits one block, the 257th token
+    starts the second) on a block table of the test's own choosing: the
+    newest token lands in the last of the sequence's blocks, at the offset
+    the fact implies (the last row of block 0; the first row of block 1)."""
+    table = [5, 9]  # arbitrary physical blocks, not from the page
     for ex in _golden()["block_boundary_examples"]:
-        for seq_len, slot in ex["decode_cases"]:
-            assert oracle.decode_slot(ex["block_table"], seq_len, ex["block_size"]) == slot
+        bsz = ex["block_size"]
+        for c in ex["cases"]:
+            slot = oracle.decode_slot(table, c["seq_len"], bsz)
+            block, offset = divmod(slot, bsz)
+            assert block == table[c["blocks"] - 1], ex["cite"]
+            assert offset == c["seq_len"] - 1 - (c["blocks"] - 1) * bsz, ex["cite"]
+            assert (offset == bsz - 1) == (c["blocks"] == 1)
 
 
 def _decode_slot_last_block_form(block_table, seq_len, block_size):
