@@ -1,43 +1,68 @@
-"""Reference BlockManager: block pool, reference counts and chained-hash
-prefix cache, in plain Python.
+"""Reference block allocator with a chained-hash prefix cache, in plain Python.
 
 TEST INFRASTRUCTURE ONLY (see the package docstring). The product's native
 allocator (``csrc/block_manager.cpp``) is checked against this module.
 
-It follows "12. 推理加速(二): nano-vllm — 1200 行手写 vLLM", §12.8, and the
-worked trace of "对照 Nano-vLLM 实现：读懂 vLLM 调度", §1.2. The state is:
-  * per block: reference count, prefix hash (None = not hashed), token ids;
-  * a FIFO of free block ids (taken from the front, returned to the back);
-  * the set of used block ids (exactly the blocks with ref_count > 0);
-  * a map from prefix hash to block id (the prefix-cache index).
-A block's hash covers the whole prefix up to and including the block: it
-hashes the previous block's hash (8 bytes, little endian; nothing for the
-first block) followed by the block's token ids as int64 little endian, with
-xxh64 (seed 0). Only full blocks are hashed. Freeing a block keeps its hash
-and its index entry, so a later request can revive it; the stale entry is
-dropped only when the block is handed out again.
+What it models ("12. 推理加速(二): nano-vllm — 1200 行手写 vLLM", §12.8, the
+block manager's behaviour; "对照 Nano-vLLM 实现：读懂 vLLM 调度", §1.2, the
+worked trace that pins it), written as a state and the rules that every
+operation keeps, not as a transcription of the page's code:
+
+State
+  * ``holders[b]``: how many live sequences have block ``b`` in their table
+    (the reference count; 0 for a free block).
+  * ``free_order``: the free blocks, in the order they became free (all
+    blocks, ascending, at the start). Fresh blocks are taken from its front.
+  * ``content[b]``: for a block that was filled and hashed, the pair
+    (prefix hash, token ids); absent otherwise.
+  * ``lookup``: prefix hash -> block, the cache index.
+
+Rules
+  R1 (prefix hash) The hash of block i of a token sequence covers the whole
+     prefix: xxh64 (seed 0) over the hash of block i-1 as 8 little-endian
+     bytes (nothing for block 0) followed by block i's token ids as int64
+     little endian. Only full blocks are hashed.
+  R2 (cache hit) A prompt's cached prefix is the longest run of leading
+     blocks, never including its last block, whose prefix hashes are in
+     ``lookup`` with stored tokens equal to the prompt's (a hash collision
+     is not a hit).
+  R3 (admission) A prompt fits when the free pool holds one block for every
+     block of the prompt that is not a hit held by a live sequence (a hit
+     that sits in the free pool still uses a free slot: it is taken out).
+  R4 (allocation) The table is the hit blocks, in order (each held once
+     more; a free one leaves the free pool), followed by fresh blocks from
+     the front of ``free_order``. A fresh block loses its old content and,
+     if ``lookup`` still names it, that index entry.
+  R5 (release) A finished sequence lets go of its blocks last to first;
+     each block nobody holds any more joins the back of ``free_order``,
+     keeping its content and index entry (a later prompt may revive it).
+  R6 (growth) A decoding sequence whose length is one past a multiple of the
+     block size has spilled into a new block: one fresh block (R4) is
+     appended, and admission requires one free block.
+  R7 (hashing) After a step, every block that the computed tokens have now
+     filled, and that was not full before the step, gets its prefix hash
+     and tokens recorded, and ``lookup`` maps that hash to it.
 
 Sequences are plain objects held by the caller: ``token_ids`` (the whole
-sequence so far), ``block_table`` and ``num_cached_tokens``.
+sequence so far), ``block_table`` and ``num_cached_tokens``. The method
+names are the page's (they are the interface the trace drives).
 """
 
 from __future__ import annotations
 
-from collections import deque
 from dataclasses import dataclass, field
+from itertools import takewhile
 
 import numpy as np
 import xxhash
 
 
 def chained_hash(token_ids, prefix: int | None) -> int:
-    """xxh64 of (prefix hash as 8 little-endian bytes, if any) + the tokens as
-    int64 little-endian bytes ([P1 §12.8] compute_hash)."""
-    h = xxhash.xxh64(seed=0)
-    if prefix is not None:
-        h.update(int(prefix).to_bytes(8, "little"))
-    h.update(np.asarray(token_ids, dtype="<i8").tobytes())
-    return h.intdigest()
+    """R1 for one block: xxh64 of (prefix hash as 8 little-endian bytes, if
+    any) + the tokens as int64 little-endian bytes."""
+    data = b"" if prefix is None else int(prefix).to_bytes(8, "little")
+    data += np.asarray(token_ids, dtype="<i8").tobytes()
+    return xxhash.xxh64_intdigest(data, seed=0)
 
 
 @dataclass
@@ -58,123 +83,97 @@ class Seq:
         return self.token_ids[i * self.block_size:(i + 1) * self.block_size]
 
 
+def prefix_hashes(seq: Seq, n_blocks: int) -> list:
+    """R1 over the first n_blocks blocks of a sequence."""
+    out, h = [], None
+    for i in range(n_blocks):
+        h = chained_hash(seq.block(i), h)
+        out.append(h)
+    return out
+
+
 class BlockManager:
     def __init__(self, num_blocks: int, block_size: int):
         self.block_size = block_size
-        self.ref_count = [0] * num_blocks
-        self.hash: list = [None] * num_blocks
-        self.tokens: list = [[] for _ in range(num_blocks)]
-        self.free = deque(range(num_blocks))
-        self.used: set = set()
-        self.index: dict = {}
+        self.holders = [0] * num_blocks
+        self.free_order = list(range(num_blocks))
+        self.content: dict = {}
+        self.lookup: dict = {}
 
-    # -- single blocks --------------------------------------------------
-    def _take_free_block(self) -> int:
-        """Hand out the block at the front of the free FIFO; drop its stale
-        index entry if the index still points at it; reset it (count 1, no
-        hash, no tokens)."""
-        bid = self.free.popleft()
-        assert self.ref_count[bid] == 0
-        old = self.hash[bid]
-        if old is not None and self.index.get(old) == bid:
-            del self.index[old]
-        self.ref_count[bid] = 1
-        self.hash[bid] = None
-        self.tokens[bid] = []
-        self.used.add(bid)
-        return bid
+    # -- R2 / R3 -------------------------------------------------------------
+    def _hits(self, seq: Seq) -> list:
+        """Blocks of the cached prefix (R2), in order."""
+        candidates = prefix_hashes(seq, seq.num_blocks - 1)
 
-    def _release_block(self, bid: int) -> None:
-        """Return an unreferenced block to the back of the FIFO, keeping its
-        hash and index entry."""
-        assert self.ref_count[bid] == 0
-        self.used.remove(bid)
-        self.free.append(bid)
-
-    # -- prefill ----------------------------------------------------------
-    def _cached_prefix(self, seq: Seq):
-        """Walk the full blocks except the last: count leading blocks whose
-        chained hash is indexed and whose stored tokens match (collision
-        guard). Returns (hits, how many of them are in use right now)."""
-        h = None
-        hits, in_use = 0, 0
-        for i in range(seq.num_blocks - 1):
-            toks = seq.block(i)
-            h = chained_hash(toks, h)
-            bid = self.index.get(h)
-            if bid is None or self.tokens[bid] != list(toks):
-                break
-            hits += 1
-            if bid in self.used:
-                in_use += 1
-        return hits, in_use
+        def hit(i_h):
+            i, h = i_h
+            b = self.lookup.get(h)
+            return b is not None and self.content[b][1] == list(seq.block(i))
+        return [self.lookup[h] for _, h in takewhile(hit, enumerate(candidates))]
 
     def can_allocate(self, seq: Seq) -> int:
-        """Number of leading cached blocks, or -1 if the free pool cannot
-        hold the blocks that are neither cached-and-in-use nor free-revivable
-        (a cached block that sits in the free pool still takes a free slot)."""
-        hits, in_use = self._cached_prefix(seq)
-        need = seq.num_blocks - in_use
-        if len(self.free) < need:
-            return -1
-        return hits
+        """Number of cached leading blocks, or -1 if the prompt does not fit
+        (R3)."""
+        hits = self._hits(seq)
+        held = sum(1 for b in hits if self.holders[b] > 0)
+        return len(hits) if len(self.free_order) >= seq.num_blocks - held else -1
+
+    # -- R4 ------------------------------------------------------------------
+    def _fresh(self) -> int:
+        b = self.free_order.pop(0)
+        old = self.content.pop(b, None)
+        if old is not None and self.lookup.get(old[0]) == b:
+            del self.lookup[old[0]]
+        self.holders[b] = 1
+        return b
 
     def allocate(self, seq: Seq, num_cached_blocks: int) -> None:
         assert not seq.block_table
-        h = None
-        for i in range(num_cached_blocks):
-            h = chained_hash(seq.block(i), h)
-            bid = self.index[h]
-            if bid in self.used:
-                self.ref_count[bid] += 1
-            else:  # freed but not yet reused: revive it
-                self.ref_count[bid] = 1
-                self.free.remove(bid)
-                self.used.add(bid)
-            seq.block_table.append(bid)
-        for _ in range(num_cached_blocks, seq.num_blocks):
-            seq.block_table.append(self._take_free_block())
+        hits = self._hits(seq)[:num_cached_blocks]
+        assert len(hits) == num_cached_blocks
+        for b in hits:
+            if self.holders[b] == 0:
+                self.free_order.remove(b)  # revived from the free pool
+            self.holders[b] += 1
+        seq.block_table = hits + [self._fresh() for _ in range(seq.num_blocks - len(hits))]
         seq.num_cached_tokens = num_cached_blocks * self.block_size
 
+    # -- R5 ------------------------------------------------------------------
     def deallocate(self, seq: Seq) -> None:
-        for bid in reversed(seq.block_table):
-            self.ref_count[bid] -= 1
-            if self.ref_count[bid] == 0:
-                self._release_block(bid)
-        seq.num_cached_tokens = 0
+        for b in seq.block_table[::-1]:
+            self.holders[b] -= 1
+            if self.holders[b] == 0:
+                self.free_order.append(b)
         seq.block_table.clear()
+        seq.num_cached_tokens = 0
 
-    # -- decode -----------------------------------------------------------
+    # -- R6 ------------------------------------------------------------------
+    def _spilled(self, seq: Seq) -> bool:
+        return len(seq) % self.block_size == 1
+
     def can_append(self, seq: Seq) -> bool:
-        """A sequence whose length is 1 more than a multiple of the block
-        size has just spilled into a new block and needs one free block."""
-        return len(self.free) >= (1 if len(seq) % self.block_size == 1 else 0)
+        return len(self.free_order) >= int(self._spilled(seq))
 
     def may_append(self, seq: Seq) -> None:
-        if len(seq) % self.block_size == 1:
-            seq.block_table.append(self._take_free_block())
+        if self._spilled(seq):
+            seq.block_table.append(self._fresh())
 
-    # -- after a step ---------------------------------------------------------
+    # -- R7 ------------------------------------------------------------------
     def hash_blocks(self, seq: Seq, num_scheduled_tokens: int) -> None:
-        """Hash and index the blocks that the step filled: those wholly
-        inside [0, num_cached_tokens + num_scheduled_tokens) and not inside
-        [0, num_cached_tokens)."""
         bs = self.block_size
-        start = seq.num_cached_tokens // bs
-        end = (seq.num_cached_tokens + num_scheduled_tokens) // bs
-        if start == end:
-            return
-        h = self.hash[seq.block_table[start - 1]] if start > 0 else None
-        for i in range(start, end):
-            bid = seq.block_table[i]
-            toks = seq.block(i)
-            h = chained_hash(toks, h)
-            self.hash[bid] = h
-            self.tokens[bid] = list(toks)
-            self.index[h] = bid
+        full_before = seq.num_cached_tokens // bs
+        full_after = (seq.num_cached_tokens + num_scheduled_tokens) // bs
+        hashes = prefix_hashes(seq, full_after)
+        for i in range(full_before, full_after):
+            b = seq.block_table[i]
+            self.content[b] = (hashes[i], list(seq.block(i)))
+            self.lookup[hashes[i]] = b
 
-    # -- inspection -------------------------------------------------------------
+    # -- inspection ------------------------------------------------------------
     def state(self) -> dict:
-        return {"free": list(self.free), "used": sorted(self.used),
-                "ref_count": list(self.ref_count), "hash": list(self.hash),
-                "index": dict(self.index)}
+        return {"free": list(self.free_order),
+                "used": [b for b, n in enumerate(self.holders) if n > 0],
+                "ref_count": list(self.holders),
+                "hash": [self.content[b][0] if b in self.content else None
+                         for b in range(len(self.holders))],
+                "index": dict(self.lookup)}
