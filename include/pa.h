@@ -21,7 +21,8 @@
  *   - Pointers named as device pointers must point to device memory (or
  *     memory the device can read); host pointers to host memory. The caller
  *     owns every buffer. The library never allocates or frees memory; its only
- *     global state is a per-thread error message.
+ *     global state is a per-thread error message (and, for
+ *     pa_decode_noalloc, one device array per GPU that the library holds).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream). Every
  *     device entry point only enqueues work on it and returns; nothing
  *     synchronises.
@@ -155,6 +156,24 @@ int pa_decode_partitioned(const void* q, const void* k_cache, const void* v_cach
                           const pa_desc* desc, void* stream);
 size_t pa_decode_workspace_size_ex(const pa_desc* desc, int32_t num_seqs,
                                    int32_t max_context_len, int32_t partition_blocks);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops and harnesses
+ * that forbid hipMalloc. Same arguments, result and kernels as pa_decode,
+ * minus the workspace: the call uses the library's own device array of
+ * PA_NOALLOC_SCRATCH_BYTES (64 MiB; each GPU the library runs on holds one
+ * until the process ends) and allocates nothing. A batch whose
+ * pa_decode_workspace_size exceeds that returns PA_ERR_WORKSPACE before
+ * anything is launched. Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race and
+ * must not be made. The array's contents between calls do not matter.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                      float scale, void* out, const pa_desc* desc, void* stream);
 
 /*
  * pa_decode_step -- one decode step in one pass: pa_store_kv of each

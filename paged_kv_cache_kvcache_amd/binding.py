@@ -31,7 +31,7 @@ EXPORTS = (
     "pa_bm_create", "pa_bm_destroy", "pa_bm_chained_hash", "pa_bm_can_allocate", "pa_bm_allocate",
     "pa_bm_deallocate", "pa_bm_can_append", "pa_bm_may_append", "pa_bm_hash_blocks",
     "pa_bm_num_free", "pa_bm_free_list", "pa_bm_block_state", "pa_bm_lookup",
-    "pa_bm_index_entries",
+    "pa_bm_index_entries", "pa_decode_noalloc",
 )
 
 
@@ -79,6 +79,8 @@ def load():
     lib.pa_decode_workspace_size_ex.restype = sz
     lib.pa_decode.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, f32, vp, vp, sz, pdesc, vp]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, f32, vp, pdesc, vp]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_decode_partitioned.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, f32, vp, vp, sz, i32,
                                           pdesc, vp]
     lib.pa_decode_partitioned.restype = ctypes.c_int
@@ -239,6 +241,35 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
                                          _stream(q)))
     else:  # the library's partition choice: the plain entry point
         _check(lib.pa_decode(*args, ctypes.byref(desc), _stream(q)))
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float, out,
+                      max_context_len: int | None = None) -> None:
+    """pa_decode with the library's own device scratch array as workspace
+    (nothing is allocated; overlapping calls on one GPU race)."""
+    import torch
+    _need_cuda(q, k_cache, v_cache, block_tables, context_lens, out)
+    _check_cache_pair(k_cache, v_cache)
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bf16")
+    if not (q.is_contiguous() and out.is_contiguous() and block_tables.is_contiguous()
+            and context_lens.is_contiguous()):
+        raise ValueError("q, out, block_tables and context_lens must be contiguous")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    batch, h_q, d = q.shape
+    if tuple(out.shape) != (batch, h_q, d) or d != k_cache.shape[3]:
+        raise ValueError("shape mismatch between q, out and the cache")
+    if block_tables.dim() != 2 or block_tables.shape[0] != batch or context_lens.numel() != batch:
+        raise ValueError("block_tables must be [batch, max_blocks], context_lens [batch]")
+    max_blocks = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = max_blocks * int(k_cache.shape[1])
+    desc = _desc_from_cache(k_cache, h_q)
+    _check(load().pa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                    block_tables.data_ptr(), max_blocks, context_lens.data_ptr(),
+                                    batch, int(max_context_len), float(scale), out.data_ptr(),
+                                    ctypes.byref(desc), _stream(q)))
 
 
 def pa_decode_step(q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens,

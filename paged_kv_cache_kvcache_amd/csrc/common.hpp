@@ -59,12 +59,14 @@ struct NewTokens {  // the fused store's inputs (null for plain decode)
 
 // Split-K decode of num_seqs rows; lengths from context_lens, or (when it is
 // null) from cu_k[b+1] - cu_k[b]. Validates its arguments; returns a status.
+// use_scratch: the workspace is the library's own device array (the caller's
+// workspace arguments are ignored), refused if the batch needs more.
 int launch_decode(const char* who, const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_tables, int32_t max_blocks_per_seq,
                   const int32_t* context_lens, const int32_t* cu_k, int32_t num_seqs,
                   int32_t max_context_len, float scale, void* out, void* workspace,
                   size_t workspace_bytes, int32_t partition_blocks, const pa_desc* desc,
-                  void* stream, const NewTokens* nt);
+                  void* stream, const NewTokens* nt, bool use_scratch = false);
 size_t decode_workspace_bytes(const pa_desc* desc, int32_t num_seqs, int32_t max_context_len);
 
 // ------------------------------------------------------------- bf16 bits

@@ -45,6 +45,7 @@
 //     per-wave LDS region (compute_chunk_mf). Loads, pipeline and dispatch
 //     are the same.
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1302,6 +1303,42 @@ Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part
   return p;
 }
 
+// Workspace in a library-owned device array, for callers that cannot
+// allocate (pa_decode_noalloc). Each GPU the library runs on holds its own
+// copy of the array until the process ends; every call on that GPU shares
+// it, so calls that overlap on one GPU race. The decode kernels write every
+// workspace byte they later read (dispatch order, chosen partition length,
+// partials), so nothing has to start at zero.
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;  // per GPU
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of this device's `scratch` (its host-side name is only a
+// stand-in and is never passed to a kernel), looked up once per device with
+// that device current.
+int scratch_address(const char* who, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PA_ERR_UNSUPPORTED, "%s: device %d beyond %d", who, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PA_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 }  // namespace
 
 int launch_decode(const char* who, const void* q, const void* k_cache, const void* v_cache,
@@ -1310,7 +1347,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
                   int32_t max_context_len,
                   float scale, void* out, void* workspace, size_t workspace_bytes,
                   int32_t partition_blocks, const pa_desc* desc, void* stream,
-                  const NewTokens* nt) {
+                  const NewTokens* nt, bool use_scratch) {
   int rc = check_desc(desc);
   if (rc) return rc;
   if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 0 || partition_blocks < 0)
@@ -1343,6 +1380,20 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
                   "%s: k_new/v_new need 16-byte aligned rows with stride >= H_kv*d", who);
   }
   const Plan plan = make_plan(desc, num_seqs, max_context_len, partition_blocks);
+  if (use_scratch) {  // the library's array replaces the caller's workspace
+    if (plan.ws_bytes > kScratchBytes)
+      return fail(PA_ERR_WORKSPACE,
+                  "%s: this batch needs %zu bytes of workspace; the library's scratch holds %zu "
+                  "(use pa_decode with a caller-owned workspace)", who, plan.ws_bytes,
+                  kScratchBytes);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (plan.ws_bytes) {
+      rc = scratch_address(who, &workspace);
+      if (rc) return rc;
+      workspace_bytes = kScratchBytes;
+    }
+  }
   if (plan.ws_bytes) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
       return fail(PA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", who,
@@ -1503,4 +1554,15 @@ extern "C" int pa_decode_step(const void* q, const void* k_new, int64_t k_row_st
                            max_blocks_per_seq, context_lens, nullptr, num_seqs, max_context_len,
                            scale,
                            out, workspace, workspace_bytes, 0, desc, stream, &nt);
+}
+
+
+extern "C" int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t max_context_len, float scale, void* out,
+                                 const pa_desc* desc, void* stream) {
+  return pa::launch_decode("pa_decode_noalloc", q, k_cache, v_cache, block_tables,
+                           max_blocks_per_seq, context_lens, nullptr, num_seqs, max_context_len,
+                           scale, out, nullptr, 0, 0, desc, stream, nullptr, true);
 }

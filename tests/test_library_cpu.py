@@ -223,3 +223,23 @@ def test_long_partitions_are_cut_to_the_longest_context(lib):
     assert lib.pa_decode(fake, fake, fake, fake, 2 ** 22 + 1, fake, 4, 2 ** 30 + 1, 0.125, fake,
                          None, 0, ctypes.byref(_desc(bsz=1024)), None) == B.PA_ERR_INVALID_ARG
     assert b"max_context_len" in lib.pa_last_error()
+
+
+def test_noalloc_refuses_batches_beyond_its_scratch_before_any_device_call(lib):
+    """pa_decode_noalloc's workspace is the library's 64 MiB device array: a
+    batch that needs more is refused on the host (no GPU needed to see it),
+    after the usual argument checks."""
+    d = _desc()
+    fake = ctypes.c_void_p(0x1000)
+    need = lib.pa_decode_workspace_size(ctypes.byref(d), 2048, 16384)
+    assert need > 64 << 20
+    assert lib.pa_decode_noalloc(fake, fake, fake, fake, 64, fake, 2048, 16384, 0.125, fake,
+                                 ctypes.byref(d), None) == B.PA_ERR_WORKSPACE
+    msg = lib.pa_last_error().decode()
+    assert "pa_decode_noalloc" in msg and str(need) in msg and str(64 << 20) in msg
+    assert lib.pa_decode_noalloc(fake, fake, fake, fake, 64, fake, 2048, 16384, -1.0, fake,
+                                 ctypes.byref(d), None) == B.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_noalloc(None, None, None, None, 0, None, 0, 0, 1.0, None,
+                                 ctypes.byref(d), None) == 0  # empty batch: no-op
+    # the Qwen3-8B decode batch fits
+    assert lib.pa_decode_workspace_size(ctypes.byref(d), 256, 8192) <= 64 << 20
