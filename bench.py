@@ -9,8 +9,13 @@ Inputs are seeded synthetic data already resident in HBM when timing starts.
 Prints ONE JSON line: the metric (KV GB/s of the step's algorithmic bytes,
 with % of HBM peak and tokens/s beside it), the roofline of the dominant
 call (pa_decode) timed with HIP events on its stream, and the CPU oracle
-baseline on a bounded sample. ``--prefill`` adds the varlen prefill
-workload (MFMA) as an extra object.
+baseline on a bounded sample. A default run adds, under "configs", the
+other workloads with their own rooflines and CPU baselines: the
+Qwen3-0.6B-shaped decode (64 sequences, U[128, 4096]), the long-context
+decode (32 x 16,384) and the prefix-cached prefill (bf16 MFMA roofline)
+with its 18,342-token store (HBM roofline). ``--only`` times the headline
+workload alone and ``--prefill-only`` the prefill workload alone (for
+profiling one workload).
 """
 
 from __future__ import annotations
@@ -36,8 +41,10 @@ def pmc_decode_file(config: str) -> str:
     """The committed counter record of a decode workload (may not exist)."""
     return os.path.join(ROOT, "profiles", "pmc_decode_%s.json" % config)
 PMC_PREFILL_FILE = os.path.join(ROOT, "profiles", "pmc_prefill_prefix1024.json")
+PMC_STORE_FILE = os.path.join(ROOT, "profiles", "pmc_store_prefill18k.json")
 DECODE_SRC = os.path.join(ROOT, "paged_kv_cache_kvcache_amd", "csrc", "decode.hip")
 PREFILL_SRC = os.path.join(ROOT, "paged_kv_cache_kvcache_amd", "csrc", "prefill.hip")
+STORE_SRC = os.path.join(ROOT, "paged_kv_cache_kvcache_amd", "csrc", "store_kv.hip")
 
 
 def decode_bytes(case) -> int:
@@ -105,56 +112,98 @@ def _oracle_rows(rows):
     return len(rows)
 
 
+def _oracle_prefill_piece(task):
+    """Worker: the oracle's prefill of query rows [lo, hi) of sequence b."""
+    import oracle
+    b, lo, hi = task
+    c, cu_q = _CPU_CASE, _CPU_CU_Q
+    q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+    oracle.prefill_one(c.q[q0:q1], c.k_cache, c.v_cache, c.block_tables[b], int(c.ends[b]),
+                       c.scale, query_rows=range(lo, hi))
+    return task
+
+
 _CPU_CASE = None
+_CPU_CU_Q = None
 
 
 def cpu_baseline_child(args) -> int:
     """Runs in a fresh interpreter that never touches the GPU: draws the same
-    workload and times the fp64 oracle's decode of its sequences in a pool of
-    worker processes, one per host core (at most 16, one thread each), until
-    the batch is done or about ``--cpu-budget`` seconds have passed."""
+    workload and times the fp64 oracle on it in a pool of worker processes,
+    one per host core (at most 16, one thread each), until the batch is done
+    or about ``--cpu-budget`` seconds have passed. Decode: one sequence per
+    task, in batch order. Prefill: pieces of 64 query rows, in batch order."""
     import multiprocessing as mp
 
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from paged_kv_cache_kvcache_amd import workloads as W
-    global _CPU_CASE
+    global _CPU_CASE, _CPU_CU_Q
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
     case = W.make_case(args.config, block_size=args.block_size, threads=cores)
     _CPU_CASE = case
-    chunks = [list(range(b, min(b + 4, case.batch))) for b in range(0, case.batch, 4)]
-    done = 0
+    prefill = args.config == "prefill"
+    if prefill:
+        qlens = (case.ends - case.starts).astype(np.int64)
+        _CPU_CU_Q = np.concatenate([[0], np.cumsum(qlens)])
+        tasks = [(b, lo, min(int(qlens[b]), lo + 64)) for b in range(case.batch)
+                 for lo in range(0, int(qlens[b]), 64)]
+        fn = _oracle_prefill_piece
+    else:
+        tasks = [[b] for b in range(case.batch)]
+        fn = _oracle_rows
+    done = []
     with threadpool_limits(1):
         pool = mp.get_context("fork").Pool(cores)
         try:
             t0 = time.perf_counter()
-            for n in pool.imap(_oracle_rows, chunks):
-                done += n
+            for r in pool.imap(fn, tasks):
+                done.append(r)
                 if time.perf_counter() - t0 >= args.cpu_budget:
                     break
             el = time.perf_counter() - t0
         finally:
             pool.terminate()
-    tokens = int(case.context_lens[:done].sum())
+    if prefill:
+        # causal-exact FLOPs of the rows done: query row i of sequence b sits
+        # at position starts[b] + i and sees that many keys plus one
+        flops = 0.0
+        rows = 0
+        for b, lo, hi in done:
+            s0 = int(case.starts[b])
+            flops += prefill_flops([s0 + lo], [s0 + hi], case.num_q_heads, case.head_dim)
+            rows += hi - lo
+        total_rows = int((case.ends - case.starts).sum())
+        print(json.dumps({
+            "value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "fp64 numpy oracle prefill of %d of %d query rows (%d pieces of up to 64 "
+                      "rows, batch order) in %d worker processes of one thread each, %.2f s; "
+                      "store not included" % (rows, total_rows, len(done), cores, el),
+            "q_tokens_per_s": round(rows / el, 3)}), flush=True)
+        return 0
+    n_seqs = sum(len(r_) for r_ in tasks[:len(done)])
+    tokens = int(case.context_lens[:n_seqs].sum())
     kv = tokens * case.num_kv_heads * case.head_dim * 2 * 2
-    qo = 2 * done * case.num_q_heads * case.head_dim * 2
+    qo = 2 * n_seqs * case.num_q_heads * case.head_dim * 2
     print(json.dumps({
         "value": round((kv + qo) / el / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
         "sample": "fp64 numpy oracle decode of the first %d of %d sequences (%d context tokens) "
                   "in %d worker processes of one thread each, %.2f s; store not included" % (
-                      done, case.batch, tokens, cores, el),
-        "tokens_per_s_per_layer": round(done / el, 3)}), flush=True)
+                      n_seqs, case.batch, tokens, cores, el),
+        "tokens_per_s_per_layer": round(n_seqs / el, 3)}), flush=True)
     return 0
 
 
-def cpu_baseline(args):
-    """The CPU oracle baseline, measured in a child process (see
-    cpu_baseline_child) so that its workers fork from a process without a
-    GPU context."""
+def cpu_baseline(args, config: str):
+    """The CPU oracle baseline of one workload, measured in a child process
+    (see cpu_baseline_child) so that its workers fork from a process without
+    a GPU context."""
     import subprocess
-    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--config",
-           args.config, "--block-size", str(args.block_size), "--cpu-budget",
-           str(args.cpu_budget)]
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child",
+           "--block-size", str(args.block_size), "--cpu-budget", str(args.cpu_budget)]
+    cmd += ["--prefill-only"] if config == "prefill" else ["--config", config]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True,
                        timeout=args.cpu_budget + 600)
     if r.returncode != 0:
@@ -162,18 +211,25 @@ def cpu_baseline(args):
     return json.loads(r.stdout.strip().splitlines()[-1])
 
 
-def run_prefill(args, torch, B, W, dev):
+def _dev(torch, dev):
     import numpy as np
-    case = W.make_case("prefill")
-    slots, cu_q, cu_k = B.pa_build_metadata(case.block_tables, case.starts, case.ends,
-                                            case.block_size)
 
     def t(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     def bf(a):
         return t(a.view(np.int16)).view(torch.bfloat16)
+    return t, bf
 
+
+def run_prefill(args, torch, B, W, dev):
+    """The prefix-cached prefill workload: pa_store_kv of the 18,342 new
+    tokens, then pa_prefill_varlen. Two rooflines: the prefill kernel
+    (causal-exact FLOPs, dense bf16 MFMA peak) and the store (bytes, HBM)."""
+    case = W.make_case("prefill")
+    slots, cu_q, cu_k = B.pa_build_metadata(case.block_tables, case.starts, case.ends,
+                                            case.block_size)
+    t, bf = _dev(torch, dev)
     kc, vc = bf(case.k_cache), bf(case.v_cache)
     k_new, v_new, q = bf(case.k_new), bf(case.v_new), bf(case.q)
     out = torch.empty_like(q)
@@ -203,18 +259,31 @@ def run_prefill(args, torch, B, W, dev):
     t_store = sum(e[0].elapsed_time(e[1]) for e in ev) / n * 1e-3
     t_attn = sum(e[1].elapsed_time(e[2]) for e in ev) / n * 1e-3
     flops = prefill_flops(case.starts, case.ends, case.num_q_heads, case.head_dim)
-    sb = store_bytes(int(qlens.sum()), case.num_kv_heads, case.head_dim)
+    n_q = int(qlens.sum())
+    sb = store_bytes(n_q, case.num_kv_heads, case.head_dim)
+    tflops = flops / t_attn / 1e12
+    store_gbs = sb / t_store / 1e9
     return {
-        "workload": "prefill: 16 prompts, shared 1024-token prefix (4 blocks) + suffix "
-                    "U[100,2000], 32 q / 8 kv heads, d 128",
-        "q_tokens": int(qlens.sum()),
-        "ms_store": round(t_store * 1e3, 4), "ms_prefill": round(t_attn * 1e3, 4),
-        "store_GBps": round(sb / t_store / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(flops / t_attn / 1e12, 2),
-                     "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(flops / t_attn / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "workload": W.DESCRIPTIONS["prefill"] + "; step = store of the %d new tokens + prefill"
+                    % n_q,
+        "metric": "varlen causal prefill over paged K/V: TFLOP/s (causal-exact) and query "
+                  "tokens/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s",
+        "q_tokens": n_q,
+        "ms_per_call": {"pa_store_kv": round(t_store * 1e3, 5),
+                        "pa_prefill_varlen": round(t_attn * 1e3, 5)},
+        "q_tokens_per_s": round(n_q / (t_store + t_attn), 1),
+        "algorithmic": {"prefill_flops": flops, "store_bytes": sb},
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill_varlen (prefill_kernel)",
+                     "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic_from_profile(PMC_PREFILL_FILE, PREFILL_SRC, None)},
-        "q_tokens_per_s": round(int(qlens.sum()) / (t_store + t_attn), 1),
+        "store": {"tokens": n_q, "value": round(store_gbs, 1), "unit": "GB/s",
+                  "roofline": {"bound": "hbm", "kernel": "pa_store_kv (store_kv_vec16_kernel)",
+                               "achieved": round(store_gbs, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(store_gbs / HBM_PEAK_GBS, 4),
+                               "traffic": traffic_from_profile(PMC_STORE_FILE, STORE_SRC,
+                                                               None)}},
     }
 
 
@@ -275,70 +344,15 @@ def run_mixed(args, torch, B, W, dev):
             "ms_per_step_single_prefill_launch": round(ms_single, 4)}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="qwen3-8b",
-                    choices=["qwen3-8b", "qwen3-0.6b", "long", "gqa8", "gqa16"])
-    ap.add_argument("--cpu-budget", type=float, default=15.0,
-                    help="seconds of oracle work for the CPU baseline (0 = skip)")
-    ap.add_argument("--prefill", action="store_true", help="also time the prefill workload")
-    ap.add_argument("--mixed", action="store_true",
-                    help="also time a mixed decode + chunked-prefill varlen step")
-    ap.add_argument("--mode", default="separate", choices=["fused", "separate"],
-                    help="fused: pa_decode_step (store + decode in one pass); separate: "
-                         "pa_store_kv then pa_decode")
-    ap.add_argument("--graph", action="store_true",
-                    help="capture the step in a HIP graph and time its replays")
-    ap.add_argument("--replicas", type=int, default=0,
-                    help="copies of the KV pool read in turn by consecutive steps (0: 2 when "
-                         "the batch's K/V are under 2 GiB, so the last-level cache cannot serve "
-                         "a step from the previous one; 1 with --graph)")
-    ap.add_argument("--block-size", type=int, default=256,
-                    help="tokens per cache block (power of two, 16..1024); same lengths")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="only run a plain device copy of MIB MiB (counter calibration)")
-    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
-    args = ap.parse_args()
-    if args.cpu_baseline_child:
-        return cpu_baseline_child(args)
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU; --gpus %d (WORLD_SIZE %d) is not supported: the "
-              "library has no multi-GPU path" % (args.gpus, world), file=sys.stderr)
-        return 2
-
-    import numpy as np
-    import torch
-
-    from paged_kv_cache_kvcache_amd import binding as B
-    from paged_kv_cache_kvcache_amd import workloads as W
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(max(1, args.steps)):
-            dst.copy_(src)
-        torch.cuda.synchronize(dev)
-        print(json.dumps({"copy_calibration_bytes": n, "launches": max(1, args.steps)}))
-        return 0
-
-    B.load()
-    case = W.make_case(args.config, block_size=args.block_size)
-
-    def t(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    def bf(a):
-        return t(a.view(np.int16)).view(torch.bfloat16)
-
+def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
+               graph: bool = False, replicas: int = 0) -> dict:
+    """One decode workload: W untimed steps, then K steps back to back
+    between two events (the step time), then K steps again with events
+    around each call (per-call times; the roofline's). A step is
+    pa_store_kv of the batch's new tokens + pa_decode (mode "separate") or
+    pa_decode_step (mode "fused"), optionally replayed as a HIP graph."""
+    case = W.make_case(config, block_size=args.block_size)
+    t, bf = _dev(torch, dev)
     slots, _, _ = B.pa_build_metadata(case.block_tables, case.starts, case.context_lens,
                                       case.block_size)
     kc, vc = bf(case.k_cache), bf(case.v_cache)
@@ -353,7 +367,7 @@ def main() -> int:
     # would be partly served from it on back-to-back steps; consecutive steps
     # then read different copies of the pool.
     kv_bytes = decode_bytes(case)
-    replicas = 1 if args.graph else (args.replicas or (1 if kv_bytes >= (2 << 30) else 2))
+    replicas = 1 if graph else (replicas or (1 if kv_bytes >= (2 << 30) else 2))
     pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(replicas - 1)]
     turn = [0]
 
@@ -368,7 +382,7 @@ def main() -> int:
         B.pa_decode_step(q, k_new, v_new, pool[0], pool[1], slots_d, bt_d, ctx_d, case.scale, out,
                          max_context_len=max_ctx, workspace=ws)
 
-    if args.mode == "fused":
+    if mode == "fused":
         calls = [("pa_decode_step", fused)]
     else:
         calls = [("pa_store_kv", store), ("pa_decode", decode)]
@@ -387,18 +401,18 @@ def main() -> int:
         step()
     torch.cuda.synchronize(dev)
     run = step
-    if args.graph:
+    if graph:
         side = torch.cuda.Stream(device=dev)
         side.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(side):
             step()
         torch.cuda.current_stream(dev).wait_stream(side)
         torch.cuda.synchronize(dev)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
             step()
         torch.cuda.synchronize(dev)
-        run = graph.replay
+        run = g.replay
         for _ in range(args.warmup):
             run()
         torch.cuda.synchronize(dev)
@@ -431,35 +445,21 @@ def main() -> int:
     db = decode_bytes(case)
     sb = store_bytes(case.batch, case.num_kv_heads, case.head_dim)
     gbs = (db + sb) / (ms_step * 1e-3) / 1e9
-    if args.mode == "fused":
+    if mode == "fused":
         dom, dom_bytes = "pa_decode_step", db + sb
         dom_desc = "pa_decode_step (order + store fused into split-K decode + merge)"
     else:
         dom, dom_bytes = "pa_decode", db
         dom_desc = "pa_decode (order + split-K + merge)"
     dom_gbs = dom_bytes / (ms_call[dom] * 1e-3) / 1e9
-    traffic = traffic_from_profile(pmc_decode_file(args.config), DECODE_SRC, args.mode,
-                                   args.block_size, args.config)
-
+    traffic = traffic_from_profile(pmc_decode_file(config), DECODE_SRC, mode, args.block_size,
+                                   config)
     rec = {
-        "metric": "paged decode: KV GB/s (% HBM peak) + tokens/s at Qwen3-8B shape, batch 256",
-        "value": round(gbs, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": W.DESCRIPTIONS[args.config].replace(
-                       "B 256", "B %d" % case.block_size) + "; step = store of the batch's "
-                   "new tokens + decode, one layer", "global_batch": case.batch,
-                   "seq_len": max_ctx, "parallelism": "none (1 GPU)",
-                   "block_size": case.block_size, "pool_replicas": len(pools),
-                   "step_mode": args.mode + (" + hip graph" if args.graph else "")},
+        "workload": W.DESCRIPTIONS[config].replace("B 256", "B %d" % case.block_size)
+                    + "; step = store of the batch's new tokens + decode, one layer",
+        "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(ms_step, 5),
+        "global_batch": case.batch, "seq_len": max_ctx, "block_size": case.block_size,
+        "pool_replicas": len(pools), "step_mode": mode + (" + hip graph" if graph else ""),
         "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": {"per_layer": round(case.batch / (ms_step * 1e-3), 1)},
         "ms_per_call": {k: round(v, 5) for k, v in ms_call.items()},
@@ -468,17 +468,133 @@ def main() -> int:
                      "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
-    if args.config == "qwen3-8b":
+    if config == "qwen3-8b":
         rec["tokens_per_s"]["model_36_layers"] = round(
             case.batch / (LAYERS_QWEN3_8B * ms_step * 1e-3), 1)
-    if args.prefill:
-        rec["prefill"] = run_prefill(args, torch, B, W, dev)
+    return rec
+
+
+# The other decode workloads and the prefill workload, timed by a default run
+# beside the Qwen3-8B headline (each with its own roofline and CPU baseline).
+EXTRA_DECODE = ("qwen3-0.6b", "long")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="qwen3-8b",
+                    choices=["qwen3-8b", "qwen3-0.6b", "long", "gqa8", "gqa16"])
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work per CPU baseline (0 = skip)")
+    ap.add_argument("--only", action="store_true",
+                    help="time only --config (no other workloads): for profiling one workload")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill workload (its store and prefill): for profiling")
+    ap.add_argument("--mixed", action="store_true",
+                    help="also time a mixed decode + chunked-prefill varlen step")
+    ap.add_argument("--mode", default="separate", choices=["fused", "separate"],
+                    help="fused: pa_decode_step (store + decode in one pass); separate: "
+                         "pa_store_kv then pa_decode")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step in a HIP graph and time its replays")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="copies of the KV pool read in turn by consecutive steps (0: 2 when "
+                         "the batch's K/V are under 2 GiB, so the last-level cache cannot serve "
+                         "a step from the previous one; 1 with --graph)")
+    ap.add_argument("--block-size", type=int, default=256,
+                    help="tokens per cache block (power of two, 16..1024); same lengths")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
+    args = ap.parse_args()
+    if args.cpu_baseline_child:
+        if args.prefill_only:
+            args.config = "prefill"
+        return cpu_baseline_child(args)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU; --gpus %d (WORLD_SIZE %d) is not supported: the "
+              "library has no multi-GPU path" % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import torch
+
+    from paged_kv_cache_kvcache_amd import binding as B
+    from paged_kv_cache_kvcache_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_calibration_bytes": n, "launches": max(1, args.steps)}))
+        return 0
+
+    B.load()
+
+    def progress(msg):
+        print("bench: " + msg, file=sys.stderr, flush=True)
+
+    if args.prefill_only:
+        rec = run_prefill(args, torch, B, W, dev)
+        rec["cpu_baseline"] = cpu_baseline(args, "prefill") if args.cpu_budget > 0 else None
+        print(json.dumps(rec), flush=True)
+        return 0
+
+    progress("%s decode" % args.config)
+    head = run_decode(args, torch, B, W, dev, args.config, args.mode, args.graph, args.replicas)
+    torch.cuda.empty_cache()
+    rec = {
+        "metric": "paged decode: KV GB/s (% HBM peak) + tokens/s at Qwen3-8B shape, batch 256",
+        "value": head["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "global_batch": head["global_batch"],
+                   "seq_len": head["seq_len"], "parallelism": "none (1 GPU)",
+                   "block_size": head["block_size"], "pool_replicas": head["pool_replicas"],
+                   "step_mode": head["step_mode"]},
+    }
+    for k in ("hbm_peak_frac", "tokens_per_s", "ms_per_call", "algorithmic_bytes", "roofline"):
+        rec[k] = head[k]
+    extra = {}
+    if not args.only:
+        for config in EXTRA_DECODE:
+            if config == args.config:
+                continue
+            progress("%s decode" % config)
+            extra[config] = run_decode(args, torch, B, W, dev, config)
+            torch.cuda.empty_cache()
+        progress("prefill")
+        extra["prefill"] = run_prefill(args, torch, B, W, dev)
+        torch.cuda.empty_cache()
     if args.mixed:
+        progress("mixed")
         rec["mixed"] = run_mixed(args, torch, B, W, dev)
     if args.cpu_budget > 0:
-        rec["cpu_baseline"] = cpu_baseline(args)
+        progress("CPU oracle baselines")
+        rec["cpu_baseline"] = cpu_baseline(args, args.config)
+        for config, obj in extra.items():
+            obj["cpu_baseline"] = cpu_baseline(args, config)
     else:
         rec["cpu_baseline"] = None
+    if extra:
+        rec["configs"] = extra
     print(json.dumps(rec), flush=True)
     return 0
 

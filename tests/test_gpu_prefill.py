@@ -164,3 +164,37 @@ def test_mixed_decode_and_chunked_prefill_batch(entry):
         torch.cuda.synchronize()
         out = host_f64(o)
     check_whole_output("prefill", "mixed", out)
+
+
+@pytest.mark.parametrize("h_q,h_kv,d", [(32, 8, 128), (8, 2, 64), (24, 8, 128)])
+def test_scores_far_above_the_first_keys(h_q, h_kv, d):
+    """Keys grow along each sequence (factor 1 .. 10): late keys score tens
+    of units above a column's first 32 keys, far beyond the range the
+    weights may span, so the kernel must notice and redo the columns with
+    their exact maxima. V is scaled by 1/4 (exact in bf16): the softmax is
+    then close to one-hot and an output is close to one V row, and the
+    bf16 rounding of an output near 4 alone (half an ulp: 0.0156) would
+    exceed the 1e-2 bound. Every row vs the oracle."""
+    prefix = [0, 300, 1000]
+    suffix = [200, 129, 700]
+    case = ragged_case(h_q, h_kv, d, prefix, suffix, seed=95 + d)
+    kf = oracle.bf16_bits_to_f64(case.k_cache)
+    knew = oracle.bf16_bits_to_f64(case.k_new)
+    row = 0
+    for b in range(len(prefix)):
+        end = int(case.ends[b])
+        for p in range(end):
+            f = 1.0 + 9.0 * p / end
+            if p < prefix[b]:
+                kf[case.block_tables[b, p // 256], p % 256] *= f
+            else:
+                knew[row + p - prefix[b]] *= f
+        row += suffix[b]
+    case.k_cache = W.round_to_bf16_bits(kf)
+    case.k_new = W.round_to_bf16_bits(knew)
+    case.v_cache = W.round_to_bf16_bits(oracle.bf16_bits_to_f64(case.v_cache) * 0.25)
+    case.v_new = W.round_to_bf16_bits(oracle.bf16_bits_to_f64(case.v_new) * 0.25)
+    out, kref, vref, cu_q, cu_k = run_prefill_step(case)
+    ref = oracle.prefill_varlen(case.q, kref, vref, cu_q, cu_k, case.block_tables, case.scale)
+    mx, mean = assert_close(out, ref, "growing keys %d/%d/%d" % (h_q, h_kv, d))
+    print("  parity: max abs %.3g mean abs %.3g" % (mx, mean))
