@@ -1,0 +1,185 @@
+"""CPU checks of the decode kernels' index arithmetic (csrc/decode.hip),
+re-stated here and run on every lane, chunk position and item:
+
+* matrix-core decode (compute_chunk_mf): the K rows and the V^T token pairs
+  that each lane writes to its wave's LDS region are exactly what the MFMA
+  operand reads expect: every K operand lane reads one token row's 8
+  consecutive elements, the S^T accumulator's (tile, lane group, register)
+  is the token the kernel masks and weights, and every V^T operand element
+  is V[token][d] for the token the P^T operand holds at that k-index; no
+  two writes overlap;
+* dispatch order (decode_order_kernel): whatever order the rank atomics are
+  taken in, the written order is a permutation of the work items (each
+  (sequence, partition) once, -1 after them), never written outside the
+  array, laid out as a snake over rounds of one item per CU.
+"""
+
+import numpy as np
+import pytest
+
+
+def mf_layout(D):
+    LPT, U, ROW = D // 8, D // 16, 2 * D
+    TILE = 16 * ROW
+    VROW = 80
+    VT = 2 * 16 * 2 * D  # V^T region after two K tiles
+    TPI = 64 // LPT      # tokens per load instruction
+
+    def token_of_load(u, r):
+        return u * TPI + r
+
+    mem = {}
+
+    def put(addr, label):
+        assert addr not in mem, "two writes to byte %d" % addr
+        assert 0 <= addr < VT + D * VROW
+        mem[addr] = label
+
+    for lane in range(64):
+        r, s = lane // LPT, lane % LPT
+        for u in range(U):
+            T = u >> 2 if D == 128 else r >> 2
+            rho = 4 * r + (u & 3) if D == 128 else 4 * (r & 3) + u
+            base = T * TILE + rho * ROW + ((s ^ (rho & (LPT - 1))) << 4)
+            for e in range(8):
+                put(base + 2 * e, ("K", token_of_load(u, r), 8 * s + e))
+        for w in range(4):
+            for e in range(2):
+                d = 8 * s + 2 * w + e
+                if D == 128:
+                    base = VT + d * VROW + ((r ^ ((d >> 4) & 3)) << 4)
+                    for u in range(8):  # bf16 element u of the 16 bytes
+                        put(base + 2 * u, ("V", token_of_load(u, r), d))
+                else:
+                    base = VT + d * VROW + (((r & 3) ^ ((d >> 4) & 3)) << 4) + 8 * (r >> 2)
+                    for u in range(4):
+                        put(base + 2 * u, ("V", token_of_load(u, r), d))
+    return mem, LPT, ROW, TILE, VROW, VT
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_matrix_core_chunk_layout_agrees(D):
+    mem, LPT, ROW, TILE, VROW, VT = mf_layout(D)
+
+    def score_token(T, g, c):  # the token the kernel masks for (tile, group, register)
+        return 16 * T + 4 * c + g if D == 128 else 8 * c + 4 * T + g
+
+    seen_tokens = set()
+    for T in range(2):
+        row_token = {}
+        for j in range(D // 32):
+            for lane in range(64):
+                g, i = lane >> 4, lane & 15
+                base = T * TILE + i * ROW + (((4 * j + g) ^ (i & (LPT - 1))) << 4)
+                labels = [mem[base + 2 * e] for e in range(8)]
+                toks = {lab[1] for lab in labels}
+                assert len(toks) == 1 and labels[0][0] == "K"
+                assert [lab[2] for lab in labels] == [32 * j + 8 * g + e for e in range(8)]
+                tok = toks.pop()
+                assert row_token.setdefault(i, tok) == tok  # row i is one token throughout
+        # the S^T accumulator: lane (g, i), register c holds tile row 4g + c
+        for g in range(4):
+            for c in range(4):
+                assert row_token[4 * g + c] == score_token(T, g, c)
+                seen_tokens.add(score_token(T, g, c))
+    assert seen_tokens == set(range(32))
+    # V^T operand of tile mt: lane (g, i) reads d = 16 mt + i, k-index 8 g + q,
+    # which must be V[token][d] for the token P^T holds there (q = 4 T + c)
+    for mt in range(D // 16):
+        for lane in range(64):
+            g, i = lane >> 4, lane & 15
+            d = 16 * mt + i
+            base = VT + d * VROW + ((g ^ (mt & 3)) << 4)
+            for q in range(8):
+                T, c = q >> 2, q & 3
+                assert mem[base + 2 * q] == ("V", score_token(T, g, c), d)
+
+
+# ---------------------------------------------------------- dispatch order
+
+def split_parts(n, P, max_parts):
+    nn = min(n, max_parts * P)
+    return nn, (nn + P - 1) // P
+
+
+def len_bucket(length, P, buckets=32):
+    return 1 + ((length - 1) * buckets) // P
+
+
+def dispatch_slot(r, rnd, max_items):
+    k = r // rnd
+    start = k * rnd
+    ln = min(rnd, max_items - start)
+    return start + ln - 1 - (r - start) if k & 1 else r
+
+
+def emulate_order(lens, P, max_parts, rnd, rng):
+    """The rank assignment with the threads' atomics taken in a random order."""
+    max_items = len(lens) * max_parts
+    NB = 33
+    items = {}
+    for s, n in enumerate(lens):
+        if n == 0:
+            items[s] = (0, 0, 0)
+            continue
+        nn, k = split_parts(n, P, max_parts)
+        items[s] = (k - 1, 32, len_bucket(nn - (k - 1) * P, P))
+    counts = [0] * NB
+    for s in rng.permutation(len(lens)):
+        bulk, kb, kl = items[s]
+        if bulk:
+            counts[kb] += bulk
+        counts[kl] += 1
+    nxt, run = [0] * NB, 0
+    for k in range(NB - 1, -1, -1):
+        nxt[k], run = run, run + counts[k]
+    total = run
+    order = [None] * max_items
+    for s in rng.permutation(len(lens)):  # a random interleaving of the atomics
+        bulk, kb, kl = items[s]
+        if bulk:
+            pos = nxt[kb]
+            nxt[kb] += bulk
+            for j in range(bulk):
+                slot = dispatch_slot(pos + j, rnd, max_items)
+                assert 0 <= slot < max_items and order[slot] is None
+                order[slot] = (j, s)
+        pos = nxt[kl]
+        nxt[kl] += 1
+        slot = dispatch_slot(pos, rnd, max_items)
+        assert 0 <= slot < max_items and order[slot] is None
+        order[slot] = (bulk, s)
+    for r in range(total, max_items):
+        slot = dispatch_slot(r, rnd, max_items)
+        assert order[slot] is None
+        order[slot] = -1
+    return order, items, total
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_dispatch_order_is_a_permutation(seed):
+    rng = np.random.default_rng(700 + seed)
+    n = int(rng.integers(1, 600))
+    lens = rng.integers(0, 9000, size=n)
+    lens[rng.random(n) < 0.1] = 0
+    P = 256 * int(rng.choice([1, 2, 4, 8, 16]))
+    max_parts = max(1, -(-int(lens.max()) // P))
+    rnd = int(rng.choice([64, 128, 256]))
+    order, items, total = emulate_order(lens, P, max_parts, rnd, rng)
+    assert None not in order
+    want = set()
+    for s, n_ in enumerate(lens):
+        k = split_parts(int(n_), P, max_parts)[1] if n_ else 1
+        want.update((j, s) for j in range(k))
+    got = [e for e in order if e != -1]
+    assert len(got) == len(want) == total and set(got) == want
+    # longest first: ranks in bucket order (full partitions, then by length)
+    ranks = {}
+    for r in range(total):
+        ranks[order[dispatch_slot(r, rnd, max_items=len(order))]] = r
+    by_rank = sorted(want, key=lambda e: ranks[e])
+    buckets = []
+    for j, s in by_rank:
+        bulk, kb, kl = items[s]
+        buckets.append(kb if j < bulk else kl)
+    assert buckets == sorted(buckets, reverse=True)
