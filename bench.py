@@ -308,7 +308,7 @@ def run_mixed(args, torch, B, W, dev):
     mq, mk = int(qlens.max()), int(case.ends.max())
 
     n_dec = case.meta["decode_rows"]
-    ws = torch.empty(max(16, B.load().pa_mixed_workspace_size(
+    ws = torch.zeros(max(16, B.load().pa_mixed_workspace_size(
         B.ctypes.byref(B._desc_from_cache(kc, case.num_q_heads)), n_dec, mk)),
         dtype=torch.uint8, device=dev)
 
@@ -361,7 +361,7 @@ def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
     slots_d, bt_d, ctx_d = t(slots), t(case.block_tables), t(case.context_lens)
     max_ctx = int(case.context_lens.max())
     ws_bytes = B.pa_decode_workspace_size(case.num_q_heads, kc, case.batch, max_ctx)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     # A batch whose K/V fit a few times into the 256 MB last-level cache (MALL)
     # would be partly served from it on back-to-back steps; consecutive steps
@@ -476,7 +476,7 @@ def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
 
 # The other decode workloads and the prefill workload, timed by a default run
 # beside the Qwen3-8B headline (each with its own roofline and CPU baseline).
-EXTRA_DECODE = ("qwen3-0.6b", "long")
+EXTRA_DECODE = ("qwen3-0.6b", "long", "skewed")
 
 
 def main() -> int:
@@ -485,7 +485,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="qwen3-8b",
-                    choices=["qwen3-8b", "qwen3-0.6b", "long", "gqa8", "gqa16"])
+                    choices=["qwen3-8b", "qwen3-0.6b", "long", "gqa8", "gqa16", "skewed"])
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work per CPU baseline (0 = skip)")
     ap.add_argument("--only", action="store_true",

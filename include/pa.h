@@ -87,12 +87,15 @@ int pa_store_kv(const void* k, int64_t k_row_stride, const void* v, int64_t v_ro
 
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_decode needs for
- * this batch geometry: split-K partial results when a sequence can span
- * more than one partition, and a longest-first dispatch order (with the
- * partition length chosen on the device from the actual lengths, down to a
- * quarter of the host's estimate) when the grid has more work items than
- * the GPU has compute units (at most 4096 sequences). 0 when neither
- * applies, and on invalid arguments. The result depends only on the
+ * this batch geometry. Layout: a fixed 256 KiB header of arrival counters
+ * (one per sequence and kv-head; the single-launch decode counts there which
+ * pieces of a split sequence are done, so the last one merges them), then
+ * the split-K partial results (one row per range of the grid and sequence).
+ * Batches of more than 65,536 (sequence, kv-head) pairs, and explicit
+ * partition lengths (pa_decode_partitioned), use the partitioned grid
+ * instead: the same header (left untouched), partials per partition, and a
+ * longest-first dispatch order. 0 on invalid arguments, and for a
+ * partitioned grid that needs no workspace. The result depends only on the
  * arguments.
  */
 size_t pa_decode_workspace_size(const pa_desc* desc, int32_t num_seqs, int32_t max_context_len);
@@ -127,8 +130,14 @@ size_t pa_decode_workspace_size(const pa_desc* desc, int32_t num_seqs, int32_t m
  *                 maximum of the scaled scores only for a positive scale.
  *   out           device, bf16 [num_seqs, H_q, d]; must not alias inputs.
  *   workspace     device, >= pa_decode_workspace_size(...) bytes, 16-byte
- *                 aligned; may be NULL when that size is 0. Contents on entry
- *                 are ignored; overlapping calls must not share it.
+ *                 aligned; may be NULL when that size is 0. Its first 256 KiB
+ *                 (the counter header) must be zero before the first call
+ *                 that uses it (hipMemset, torch.zeros); every call leaves
+ *                 them zero again, so zeroing once per allocation is enough,
+ *                 whatever the shapes of later calls. The rest needs no
+ *                 initial value. Overlapping calls must not share it. (With
+ *                 PA_DEBUG set, a call checks the header and returns
+ *                 PA_ERR_WORKSPACE if it is not zero.)
  */
 int pa_decode(const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -145,8 +154,9 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * the dispatch order is computed). A partition longer than
  * ceil(max_context_len / 256) units is cut to that length (it already holds
  * every sequence whole). The result is the same attention for any partition
- * size up to rounding. Workspace: pa_decode_workspace_size_ex (the same
- * cut applies).
+ * size up to rounding. This runs the partitioned grid (an ordering kernel,
+ * the split kernel, a merge kernel). Workspace: pa_decode_workspace_size_ex
+ * (the same cut applies; the same header rule as pa_decode).
  */
 int pa_decode_partitioned(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -167,7 +177,8 @@ size_t pa_decode_workspace_size_ex(const pa_desc* desc, int32_t num_seqs,
  * pa_decode_workspace_size exceeds that returns PA_ERR_WORKSPACE before
  * anything is launched. Every call on one GPU shares that GPU's array:
  * calls that overlap on one GPU (other streams, other threads) race and
- * must not be made. The array's contents between calls do not matter.
+ * must not be made. The array starts zeroed (the counter header's required
+ * state) and every call leaves its header zero.
  */
 #define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
@@ -246,7 +257,8 @@ int pa_prefill_varlen(const void* q, const void* k_cache, const void* v_cache,
  *
  *   num_decode_rows  0 <= num_decode_rows <= num_seqs.
  *   workspace     device, >= pa_mixed_workspace_size(desc, num_decode_rows,
- *                 max_seqlen_k) bytes (may be NULL when that is 0).
+ *                 max_seqlen_k) bytes (may be NULL when that is 0); the
+ *                 decode rows' workspace, under pa_decode's header rule.
  */
 size_t pa_mixed_workspace_size(const pa_desc* desc, int32_t num_decode_rows,
                                int32_t max_seqlen_k);

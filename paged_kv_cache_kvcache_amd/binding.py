@@ -230,7 +230,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     need = int(lib.pa_decode_workspace_size_ex(ctypes.byref(desc), batch, int(max_context_len),
                                                int(partition_blocks)))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
@@ -304,7 +304,7 @@ def pa_decode_step(q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables
     lib = load()
     need = int(lib.pa_decode_workspace_size(ctypes.byref(desc), batch, int(max_context_len)))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.pa_decode_step(q.data_ptr(), k_new.data_ptr(), k_new.stride(0), v_new.data_ptr(),
@@ -368,7 +368,7 @@ def pa_mixed_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, num_decode_
     need = int(lib.pa_mixed_workspace_size(ctypes.byref(desc), int(num_decode_rows),
                                            int(max_seqlen_k)))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.pa_mixed_varlen(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),

@@ -46,6 +46,8 @@ int debug_check_tables(const char* who, const int32_t* block_tables, int32_t max
 int debug_check_varlen(const char* who, const int32_t* cu_q, const int32_t* cu_k,
                        int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
                        int32_t decode_rows, hipStream_t s);
+// PA_ERR_WORKSPACE unless the first `bytes` bytes at device address p are zero.
+int debug_check_zero(const char* who, const void* p, size_t bytes, hipStream_t s);
 
 // ------------------------------------------------- decode launch (decode.hip)
 

@@ -86,6 +86,8 @@ struct DecodeArgs {
   // partition length chosen by decode_order_kernel (null: part_tokens)
   int32_t* part_dev;
   int32_t group;   // q-heads per kv-head
+  int32_t max_ctx;  // host bound of the lengths (the stream grid cuts longer ones there)
+  int32_t* counters;  // stream grid: arrival count per (sequence, kv-head), zero between calls
   float scale_log2;
 };
 
@@ -175,12 +177,14 @@ __device__ __forceinline__ uint4 load16(const char* p) {
 // overlap only adds requests to already full memory queues (measured 5%
 // slower at the Qwen3-8B batch); with fewer waves it is what keeps enough
 // bytes in flight (waiting here measured up to twice as slow at one wave
-// per SIMD), so the host picks the kernel. Chunks of 4 loads never wait.
+// per SIMD), so the host picks the kernel, and a kernel built with the wait
+// may skip it at run time (`on`, wave-uniform). Chunks of 4 loads never
+// wait.
 template <int U, bool DRAIN>
-__device__ __forceinline__ void drain_loads() {
+__device__ __forceinline__ void drain_loads(bool on) {
   if constexpr (DRAIN && U == 8) {
     __builtin_amdgcn_sched_barrier(0);  // not hoisted into the multiply before it
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (on) __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 }
 
@@ -275,11 +279,10 @@ __device__ __forceinline__ float fold(float lo, float hi, bool sel) {
 // Tokens 2k and 2k+1 sit in lanes i and i^1: their weights are packed into
 // one bf16 pair there and broadcast to the row for the P.V products.
 template <class S, int D, int G, int U, bool TAIL>
-__device__ __forceinline__ void compute_chunk_t(SplitState<D, G>& st, float scale_log2, int row,
-                                                int nvalid, const uint4 (&kr)[U],
+__device__ __forceinline__ void compute_chunk_t(SplitState<D, G>& st, float scale_log2, int lane,
+                                                int row, int nvalid, const uint4 (&kr)[U],
                                                 const uint4 (&vr)[U]) {
   static_assert(S::LPT == 16 && (U == 4 || U == 8), "16-lane vectors, 4 or 8 loads");
-  const int lane = threadIdx.x;
   const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
   const int u_me = U == 8 ? (b2 ? 4 : 0) + (b1 ? 2 : 0) + (b0 ? 1 : 0) : (b2 ? 2 : 0) + (b0 ? 1 : 0);
   float sc[G];  // this lane's token's raw q.k per head
@@ -353,11 +356,11 @@ __device__ __forceinline__ void compute_chunk_t(SplitState<D, G>& st, float scal
 }
 
 template <class S, int D, int G, int U, bool TAIL>
-__device__ __forceinline__ void compute_chunk_v(SplitState<D, G>& st, float scale_log2, int row,
-                                              int nvalid, const uint4 (&kr)[U],
+__device__ __forceinline__ void compute_chunk_v(SplitState<D, G>& st, float scale_log2, int lane,
+                                              int row, int nvalid, const uint4 (&kr)[U],
                                               const uint4 (&vr)[U]) {
   if constexpr (S::LPT == 16 && (U == 4 || U == 8)) {
-    compute_chunk_t<S, D, G, U, TAIL>(st, scale_log2, row, nvalid, kr, vr);
+    compute_chunk_t<S, D, G, U, TAIL>(st, scale_log2, lane, row, nvalid, kr, vr);
     return;
   }
   float s[U][G];  // raw q.k (unscaled)
@@ -485,13 +488,12 @@ __device__ __forceinline__ float sum_pair_bf16(uint32_t pair, float acc) {
 // row d sits at g ^ ((d >> 4) & 3).
 template <int D, bool TAIL>
 __device__ __forceinline__ void compute_chunk_mf(MfState<D>& st, char* lds, float scale_log2,
-                                                 int nvalid, const uint4 (&kr)[D / 16],
+                                                 int lane, int nvalid, const uint4 (&kr)[D / 16],
                                                  const uint4 (&vr)[D / 16]) {
   constexpr int U = D / 16;          // loads per chunk (32 tokens)
   constexpr int LPT = D / 8;         // lanes per token vector (16-byte blocks per row)
   constexpr int ROW = 2 * D;         // bytes per K row
   constexpr int TILE = 16 * ROW;     // bytes per 16-token K tile
-  const int lane = threadIdx.x % kWave;
   const int g = lane >> 4, i = lane & 15;      // MFMA roles
   const int r = lane / LPT, s = lane % LPT;    // load roles: token r of an instruction, block s
   char* vt = lds + mf_kbytes(D);
@@ -597,13 +599,13 @@ __device__ __forceinline__ void compute_chunk_mf(MfState<D>& st, char* lds, floa
 // One chunk on either path: the matrix-core state takes chunks of 32 tokens
 // (a single fused token is widened to a masked chunk of copies).
 template <class L, int D, int G, int U, bool TAIL, class St>
-__device__ __forceinline__ void compute_chunk(St& st, char* lds, float scale_log2, int row,
-                                              int nvalid, const uint4 (&kr)[U],
+__device__ __forceinline__ void compute_chunk(St& st, char* lds, float scale_log2, int lane,
+                                              int row, int nvalid, const uint4 (&kr)[U],
                                               const uint4 (&vr)[U]) {
   if constexpr (std::is_same<St, MfState<D>>::value) {
     constexpr int UM = D / 16;
     if constexpr (U == UM) {
-      compute_chunk_mf<D, TAIL>(st, lds, scale_log2, nvalid, kr, vr);
+      compute_chunk_mf<D, TAIL>(st, lds, scale_log2, lane, nvalid, kr, vr);
     } else {
       uint4 kw[UM], vw[UM];
 #pragma unroll
@@ -611,10 +613,10 @@ __device__ __forceinline__ void compute_chunk(St& st, char* lds, float scale_log
         kw[u] = kr[u % U];
         vw[u] = vr[u % U];
       }
-      compute_chunk_mf<D, true>(st, lds, scale_log2, nvalid, kw, vw);
+      compute_chunk_mf<D, true>(st, lds, scale_log2, lane, nvalid, kw, vw);
     }
   } else {
-    compute_chunk_v<L, D, G, U, TAIL>(st, scale_log2, row, nvalid, kr, vr);
+    compute_chunk_v<L, D, G, U, TAIL>(st, scale_log2, lane, row, nvalid, kr, vr);
   }
 }
 
@@ -770,16 +772,38 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(DecodeArgs 
     order[dispatch_slot(r, round, max_items)] = -1;
 }
 
-// A work item is (sequence, group of KPW adjacent kv-heads, partition).
+// Partials are written and read with agent-scope atomic accesses (sc1:
+// written through to, and read from, the level where every CU of the GPU
+// sees the same data, past the per-XCD L2s), so a wave can publish its
+// partial by waiting for its own stores to complete, without a release
+// fence (which writes back the whole L2 of its XCD: about +100 us per call
+// when every wave did it) or an acquire fence (which invalidates it).
+__device__ __forceinline__ void store_agent(float* p, float x, float y) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p),
+                     __builtin_bit_cast(uint64_t, make_float2(x, y)), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float2 load_agent(const float* p) {
+  return __builtin_bit_cast(float2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// One piece of work: tokens [start, end) of sequence b (n tokens) for the
+// wave's kv-heads. `direct`: the piece is the whole sequence, and the
+// normalised output is written to out; otherwise the unnormalised partial
+// (o, m, l) goes to workspace row `slot`, q-head h at index slot * H_q + h.
 // SMALL: blocks hold fewer tokens than a chunk, so each load group looks up
 // its own block; otherwise a chunk lies inside one block.
-// Vector path (G = 1, 2, 4): one wave per workgroup (VS = 1).
+// Vector path (G = 1, 2, 4): one wave per workgroup (VS = 1), KPW adjacent
+// kv-heads per wave.
 // MF: the matrix-core variant (KPW = 1, G <= 16; G = 0 takes the group
 // size from the arguments); with VS > 1 its waves take VS adjacent kv-heads,
 // one each.
-template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1, bool MF = false>
-__global__ __launch_bounds__(kWave * VS) __attribute__((amdgpu_waves_per_eu(kSplitWavesPerSimd)))
-void decode_split_kernel(DecodeArgs a) {
+template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS, bool MF>
+__device__ __forceinline__ void decode_piece(const DecodeArgs& a, char* lds, int tid, int b,
+                                             int n, int start, int end, bool direct,
+                                             int64_t slot, bool drain_on = true) {
   static_assert(!MF || (KPW == 1 && G <= 16 && VS <= 4), "matrix-core geometry");
   static_assert(MF || G > 0, "the vector path is built per group size");
   const int Gn = G ? G : a.group;  // q-heads per kv-head
@@ -798,50 +822,28 @@ void decode_split_kernel(DecodeArgs a) {
   // kv-head groups (the host checks divisibility)
   const int n_groups = H_kv / (kPair ? VS : KPW);
   const int gw = blockIdx.x % n_groups;  // the kv-head groups of one item are adjacent
-  int b, part, P = a.part_tokens;  // P: tokens per partition
-  if (a.order) {
-    // items longest first (decode_order_kernel)
-    const int v = a.order[blockIdx.x / n_groups];
-    if (v < 0) return;
-    b = __builtin_amdgcn_readfirstlane(v & 4095);
-    part = __builtin_amdgcn_readfirstlane((v >> 12) & 4095);
-    P = part_tokens(a);  // the length the order kernel chose
-  } else {
-    // highest partition first
-    const int idx = blockIdx.x / n_groups;
-    b = idx % a.num_seqs;
-    part = a.max_parts - 1 - idx / a.num_seqs;
-  }
-  const int lane = threadIdx.x % kWave;
+  const int lane = tid % kWave;
   // which G q-heads of the kv-head (or, kPair, which kv-head of the VS)
-  const int half = VS == 1 ? 0 : threadIdx.x / kWave;
+  const int half = VS == 1 ? 0 : tid / kWave;
   const int sub = lane % LPT;                 // which 8 elements of the head vector
   const int g = kPair ? gw * VS + half : gw * KPW + (lane / LPT) % KPW;  // this lane's kv-head
   const int row = lane / SEG;                 // which token of a load instruction
-
-  const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
-  const Parts parts = split_parts(n, P, a.max_parts);
   const int64_t head0 = kPair ? (int64_t)b * H_q + (int64_t)g * Gn
                               : (int64_t)b * H_q + (int64_t)g * Gn * VS + half * Gn;  // first q-head
+  const int64_t wrow = slot * H_q + (head0 - (int64_t)b * H_q);  // its partial row
 
   if (n == 0) {  // padding row: defined as zeros, nothing read
-    if (part == 0 && row == 0) {
+    if (row == 0) {
 #pragma unroll
       for (int h = 0; h < Gn; ++h)
         *reinterpret_cast<uint4*>(a.out + (head0 + h) * D + sub * 8) = make_uint4(0, 0, 0, 0);
     }
     return;
   }
-  if (part >= parts.k) return;
-  const int start = part * P;
-  const int end = min(parts.n, start + P);
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
 
   S st;
-  char* lds = nullptr;
   if constexpr (MF) {
-    __shared__ __attribute__((aligned(16))) char mf_lds[VS * mf_bytes(D)];
-    lds = mf_lds + half * mf_bytes(D);
     // lane (g, i): q-head i (zeros past G), elements 32j + 8g .. +8
     const int qg = lane >> 4, qi = lane & 15;
 #pragma unroll
@@ -917,25 +919,25 @@ void decode_split_kernel(DecodeArgs a) {
     Lookup next = lookup(1);
     int i = 0;
     for (; i + 2 < nfull; i += 2) {
-      drain_loads<U, DRAIN>();
+      drain_loads<U, DRAIN>(drain_on);
       const Lookup after = lookup(i + 2);
       issue(next, kb, vb);  // chunk i+1
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the multiply
-      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, ka, va);
-      drain_loads<U, DRAIN>();
+      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, lane, row, CHUNK, ka, va);
+      drain_loads<U, DRAIN>(drain_on);
       next = lookup(i + 3);
       issue(after, ka, va);  // chunk i+2 (clamped)
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, kb, vb);
+      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, lane, row, CHUNK, kb, vb);
     }
     if (i + 1 < nfull) {
-      drain_loads<U, DRAIN>();
+      drain_loads<U, DRAIN>(drain_on);
       issue(next, kb, vb);  // chunk i+1
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, ka, va);
-      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, kb, vb);
+      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, lane, row, CHUNK, ka, va);
+      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, lane, row, CHUNK, kb, vb);
     } else if (i < nfull) {
-      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, row, CHUNK, ka, va);
+      compute_chunk<L, D, G, U, false>(st, lds, a.scale_log2, lane, row, CHUNK, ka, va);
     }
   }
   const int c = start + nfull * CHUNK;
@@ -950,7 +952,7 @@ void decode_split_kernel(DecodeArgs a) {
       kr[u] = load16(kc + off);
       vr[u] = load16(vc + off);
     }
-    compute_chunk<L, D, G, U, true>(st, lds, a.scale_log2, row, cend - c, kr, vr);
+    compute_chunk<L, D, G, U, true>(st, lds, a.scale_log2, lane, row, cend - c, kr, vr);
   }
   if (FUSED && end == n) {
     // the newest token: attend to it from registers and write it to its slot
@@ -959,10 +961,11 @@ void decode_split_kernel(DecodeArgs a) {
     const uint4 vt = *reinterpret_cast<const uint4*>(a.v_new + (int64_t)b * a.v_new_stride + g * D + sub * 8);
     const uint4 kr1[1] = {kt};
     const uint4 vr1[1] = {vt};
-    compute_chunk<L, D, G, 1, true>(st, lds, a.scale_log2, row, 1, kr1, vr1);
-    const int slot = a.slot_mapping[b];
-    if (row == 0 && (kPair || half == 0) && slot >= 0 && slot < (a.num_blocks << a.block_shift)) {
-      const int64_t dst = (int64_t)slot * H_kv * D + g * D + sub * 8;
+    compute_chunk<L, D, G, 1, true>(st, lds, a.scale_log2, lane, row, 1, kr1, vr1);
+    const int slot_new = a.slot_mapping[b];
+    if (row == 0 && (kPair || half == 0) && slot_new >= 0 &&
+        slot_new < (a.num_blocks << a.block_shift)) {
+      const int64_t dst = (int64_t)slot_new * H_kv * D + g * D + sub * 8;
       *reinterpret_cast<uint4*>(a.k_cache_w + dst) = kt;
       *reinterpret_cast<uint4*>(a.v_cache_w + dst) = vt;
     }
@@ -975,7 +978,7 @@ void decode_split_kernel(DecodeArgs a) {
     lt += xor_lane(lt, 16);
     lt += xor_lane(lt, 32);
     if (li < Gn) {
-      if (parts.k == 1) {
+      if (direct) {
         const float inv = 1.f / lt;
         uint16_t* dst = a.out + (head0 + li) * D + 4 * lg;
 #pragma unroll
@@ -986,32 +989,32 @@ void decode_split_kernel(DecodeArgs a) {
           *reinterpret_cast<uint2*>(dst + 16 * mt) = v;
         }
       } else {
-        const int64_t wi = (head0 + li) * a.max_parts + part;
+        const int64_t wi = wrow + li;
         float* dst = a.ws_o + wi * D + 4 * lg;
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt)
-          *reinterpret_cast<float4*>(dst + 16 * mt) =
-              make_float4(st.o[mt][0], st.o[mt][1], st.o[mt][2], st.o[mt][3]);
-        if (lg == 0) *reinterpret_cast<float2*>(a.ws_ml + wi * 2) = make_float2(st.m, lt);
+        for (int mt = 0; mt < D / 16; ++mt) {
+          store_agent(dst + 16 * mt, st.o[mt][0], st.o[mt][1]);
+          store_agent(dst + 16 * mt + 2, st.o[mt][2], st.o[mt][3]);
+        }
+        if (lg == 0) store_agent(a.ws_ml + wi * 2, st.m, lt);
       }
     }
-    return;
   } else {
     // Merge the token-rows of lanes (each has its own running max); lanes
     // SEG apart hold the same kv-head.
-  #pragma unroll
+#pragma unroll
     for (int h = 0; h < G; ++h) {
       float M = st.m[h];
-  #pragma unroll
+#pragma unroll
       for (int off = SEG; off < kWave; off <<= 1) M = fmaxf(M, xor_lane(M, off));
       const float w = (st.m[h] == -INFINITY) ? 0.f : exp2f(st.m[h] - M);
       float lh = st.l[h] * w;
-  #pragma unroll
+#pragma unroll
       for (int off = SEG; off < kWave; off <<= 1) lh += xor_lane(lh, off);
-  #pragma unroll
+#pragma unroll
       for (int e = 0; e < 8; ++e) {
         float o = st.acc[h][e] * w;
-  #pragma unroll
+#pragma unroll
         for (int off = SEG; off < kWave; off <<= 1) o += xor_lane(o, off);
         st.acc[h][e] = o;
       }
@@ -1019,9 +1022,9 @@ void decode_split_kernel(DecodeArgs a) {
       st.l[h] = lh;
     }
 
-    if (parts.k == 1) {
+    if (direct) {
       if (row == 0) {
-  #pragma unroll
+#pragma unroll
         for (int h = 0; h < G; ++h) {
           const float inv = 1.f / st.l[h];
           uint4 o;
@@ -1033,96 +1036,401 @@ void decode_split_kernel(DecodeArgs a) {
         }
       }
     } else {
-  #pragma unroll
+#pragma unroll
       for (int h = 0; h < G; ++h) {
-        const int64_t wi = (head0 + h) * a.max_parts + part;
+        const int64_t wi = wrow + h;
         if (row == 0) {
-          float4* dst = reinterpret_cast<float4*>(a.ws_o + wi * D + sub * 8);
-          dst[0] = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
-          dst[1] = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
+          float* dst = a.ws_o + wi * D + sub * 8;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) store_agent(dst + e, st.acc[h][e], st.acc[h][e + 1]);
         }
-        if (row == 0 && sub == 0)
-          *reinterpret_cast<float2*>(a.ws_ml + wi * 2) = make_float2(st.m[h], st.l[h]);
+        if (row == 0 && sub == 0) store_agent(a.ws_ml + wi * 2, st.m[h], st.l[h]);
       }
     }
   }
 }
 
-// Exact log-sum-exp merge of a sequence's partitions:
+// Exact log-sum-exp merge of the partials of one sequence, for q-heads
+// h0 .. h0+nh-1 of sequence b, partial rows slot0 .. slot0+np-1:
 // M = max m_p, L = sum l_p 2^(m_p - M), out = sum o_p 2^(m_p - M) / L.
-// One wave per (sequence, q-head), kReduceWaves per workgroup (4 measured
-// no faster than 1). The partitions are read kReduceParts at a time (one
-// round of loads for up to that many) and folded into a running max, so a
-// merge of up to kReduceParts partitions waits for memory once after the
-// length (against two passes over the partitions: 32 x 16,384 tokens
-// 336 -> 327 us per call, Qwen3-0.6B batch 87.6 -> 84.4 us).
-constexpr int kReduceWaves = 1;
-constexpr int kReduceParts = 8;
-
-template <int D>
-__global__ __launch_bounds__(kWave * kReduceWaves) void decode_reduce_kernel(DecodeArgs a,
-                                                                              int H_q) {
-  constexpr int EPL = D / kWave;  // output elements per lane
-  const int hg = (H_q + kReduceWaves - 1) / kReduceWaves;  // workgroups per sequence
-  const int h = (blockIdx.x % hg) * kReduceWaves + threadIdx.x / kWave;
-  const int b = blockIdx.x / hg;
-  if (h >= H_q) return;
-  const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
-  const int nparts = split_parts(n, part_tokens(a), a.max_parts).k;
-  if (nparts <= 1) return;
-  const int64_t w0 = ((int64_t)b * H_q + h) * a.max_parts;
+// One wave; HP (a power of two, at least nh) heads share it, 64/HP lanes
+// per head, each with D*HP/64 adjacent elements. The partials are read KP
+// at a time (one round of loads for up to that many) and folded into a
+// running max, so a merge of up to KP partials waits for memory once.
+template <int D, int HP>
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int H_q, int b, int h0, int nh,
+                                             int64_t slot0, int np) {
+  constexpr int LPH = kWave / HP;  // lanes per head
+  constexpr int EPL = D / LPH;     // elements per lane
+  static_assert(LPH >= 1 && EPL >= 1 && EPL <= 32, "merge geometry");
+  constexpr int KP = EPL >= 32 ? 1 : EPL >= 16 ? 2 : EPL >= 8 ? 4 : 8;
   const int lane = threadIdx.x % kWave;
-  float M = -INFINITY, L = 0.f;
+  const int h = lane / LPH;
+  if (h >= nh) return;
+  const int e0 = (lane % LPH) * EPL;
+  float M = -INFINITY, Lsum = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  for (int p0 = 0; p0 < nparts; p0 += kReduceParts) {
-    float2 ml[kReduceParts];
-    float src[kReduceParts][EPL];
+  for (int p0 = 0; p0 < np; p0 += KP) {
+    float2 ml[KP];
+    float src[KP][EPL];
 #pragma unroll
-    for (int k = 0; k < kReduceParts; ++k) {
-      const int p = min(p0 + k, nparts - 1);  // past the last: re-read it, weight 0 below
-      ml[k] = *reinterpret_cast<const float2*>(a.ws_ml + (w0 + p) * 2);
+    for (int k = 0; k < KP; ++k) {
+      const int p = min(p0 + k, np - 1);  // past the last: re-read it, weight 0 below
+      const int64_t wi = (slot0 + p) * H_q + h0 + h;
+      ml[k] = load_agent(a.ws_ml + wi * 2);
+      const float* s = a.ws_o + wi * D + e0;
+      if constexpr (EPL % 2 == 0) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) src[k][e] = a.ws_o[(w0 + p) * D + lane * EPL + e];
+        for (int e = 0; e < EPL; e += 2) {
+          const float2 v = load_agent(s + e);
+          src[k][e] = v.x;
+          src[k][e + 1] = v.y;
+        }
+      } else {
+        src[k][0] = __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     float Mc = M;
 #pragma unroll
-    for (int k = 0; k < kReduceParts; ++k)
-      if (p0 + k < nparts) Mc = fmaxf(Mc, ml[k].x);
+    for (int k = 0; k < KP; ++k)
+      if (p0 + k < np) Mc = fmaxf(Mc, ml[k].x);
     const float r = (M == -INFINITY) ? 0.f : exp2f(M - Mc);  // rescale what came before
-    L *= r;
+    Lsum *= r;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] *= r;
 #pragma unroll
-    for (int k = 0; k < kReduceParts; ++k) {
-      const float w = (p0 + k >= nparts || ml[k].x == -INFINITY) ? 0.f : exp2f(ml[k].x - Mc);
-      L = fmaf(ml[k].y, w, L);
+    for (int k = 0; k < KP; ++k) {
+      const float w = (p0 + k >= np || ml[k].x == -INFINITY) ? 0.f : exp2f(ml[k].x - Mc);
+      Lsum = fmaf(ml[k].y, w, Lsum);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = fmaf(src[k][e], w, o[e]);
     }
     M = Mc;
   }
-  const float inv = 1.f / L;
-  uint16_t* dst = a.out + ((int64_t)b * H_q + h) * D + lane * EPL;
-  if constexpr (EPL == 2) {
-    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(o[0] * inv, o[1] * inv);
-  } else {
+  const float inv = 1.f / Lsum;
+  uint16_t* dst = a.out + ((int64_t)b * H_q + h0 + h) * D + e0;
+  if constexpr (EPL == 1) {
     dst[0] = (uint16_t)f32_to_bf16_rne(o[0] * inv);
+  } else if constexpr (EPL == 2) {
+    *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(o[0] * inv, o[1] * inv);
+  } else if constexpr (EPL == 4) {
+    *reinterpret_cast<uint2*>(dst) =
+        make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 8) {
+      uint4 v;
+      v.x = pack_bf16x2(o[e] * inv, o[e + 1] * inv);
+      v.y = pack_bf16x2(o[e + 2] * inv, o[e + 3] * inv);
+      v.z = pack_bf16x2(o[e + 4] * inv, o[e + 5] * inv);
+      v.w = pack_bf16x2(o[e + 6] * inv, o[e + 7] * inv);
+      *reinterpret_cast<uint4*>(dst + e) = v;
+    }
   }
 }
 
-using SplitFn = void (*)(DecodeArgs);
+// ---- partitioned grid (explicit partition length, or batches too large
+// for the arrival counters): one work item per (sequence, kv-head group,
+// partition), in the order of decode_order_kernel, merged by
+// decode_reduce_kernel. Partial row of (sequence b, partition p):
+// b * max_parts + p.
+template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1, bool MF = false>
+__global__ __launch_bounds__(kWave * VS) __attribute__((amdgpu_waves_per_eu(kSplitWavesPerSimd)))
+void decode_split_kernel(DecodeArgs a, int /*unused: the stream kernel's signature*/) {
+  constexpr bool kPair = MF && VS > 1;
+  const int n_groups = a.num_kv_heads / (kPair ? VS : KPW);
+  int b, part, P = a.part_tokens;  // P: tokens per partition
+  if (a.order) {
+    // items longest first (decode_order_kernel)
+    const int v = a.order[blockIdx.x / n_groups];
+    if (v < 0) return;
+    b = __builtin_amdgcn_readfirstlane(v & 4095);
+    part = __builtin_amdgcn_readfirstlane((v >> 12) & 4095);
+    P = part_tokens(a);  // the length the order kernel chose
+  } else {
+    // highest partition first
+    const int idx = blockIdx.x / n_groups;
+    b = idx % a.num_seqs;
+    part = a.max_parts - 1 - idx / a.num_seqs;
+  }
+  const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
+  const Parts parts = split_parts(n, P, a.max_parts);
+  if (n == 0 ? part != 0 : part >= parts.k) return;
+  char* lds = nullptr;
+  if constexpr (MF) {
+    __shared__ __attribute__((aligned(16))) char mf_lds[VS * mf_bytes(D)];
+    lds = mf_lds + (VS == 1 ? 0 : threadIdx.x / kWave) * mf_bytes(D);
+  }
+  const int start = part * P;
+  decode_piece<D, G, KPW, FUSED, SMALL, DRAIN, VS, MF>(
+      a, lds, threadIdx.x, b, n, start, min(parts.n, start + P), parts.k <= 1,
+      (int64_t)b * a.max_parts + part);
+}
+
+// Merge of the partitioned grid's partials: one wave per (sequence, q-head)
+// (4 waves per workgroup measured no faster than 1).
+template <int D>
+__global__ __launch_bounds__(kWave) void decode_reduce_kernel(DecodeArgs a, int H_q) {
+  const int h = blockIdx.x % H_q;
+  const int b = blockIdx.x / H_q;
+  const int n = clamp_len(seq_len(a, b), a.max_blocks, a.block_size);
+  const int nparts = split_parts(n, part_tokens(a), a.max_parts).k;
+  if (nparts <= 1) return;
+  merge_pieces<D, 1>(a, H_q, b, h, 1, (int64_t)b * a.max_parts, nparts);
+}
+
+// ---- stream grid (the default): one launch, no dispatch order, no merge
+// kernel.
+//
+// Every sequence is cut into units of CHUNK tokens (max(1, ceil(n/CHUNK))
+// units; an empty sequence has one, which writes its zeros). For each
+// kv-head group, the units of all sequences, in batch order, are cut into W
+// contiguous grabs of equal size, one wave (workgroup) each, all resident
+// at once (one wave per SIMD), so every wave streams the same number of
+// bytes whatever the length mix: one long context among short ones is
+// spread over as many waves as its share of the bytes.
+// A grab covers the end of one sequence, whole sequences, and the start of
+// another; a sequence inside one grab is finished there, the others leave a
+// partial per grab (row j + b for grab j and sequence b: unique, since
+// grabs are consecutive intervals and consecutive sequences share at most
+// one grab), and the wave that completes a sequence's last piece merges
+// them. Completion is counted per (sequence, kv-head) in the workspace's
+// header: each wave publishes its partial (agent-scope stores, waited for)
+// and then increments the counter; the wave whose increment completes the
+// count reads the partials (agent-scope loads), merges, and sets the
+// counter back to zero, so every call leaves the header zero (the caller
+// zeroes it once).
+// What bounds it: the waves of one launch finish up to 15-25% apart, by
+// their own timestamps (the HBM fabric serves waves unevenly: XCD means
+// differ by ~8%, and CUs within an XCD more), and the launch ends with the
+// slowest. Balancing by a queue of small grabs taken with atomics, or by
+// oversubscribing the grid with smaller grabs in later levels, both
+// measured slower: each extra grab costs a chain of dependent round trips
+// (queue, lengths, table, K/V, counter) under a loaded memory system.
+// Resident waves of the split kernels on an MI355X: 256 CUs x 8 waves. A
+// fixed constant (not a device query) so the workspace size is a pure
+// function of the arguments.
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kResidentItems = kComputeUnits * 8;
+// Waves of the stream grid: one per SIMD (2 per SIMD measured 4% slower at
+// the Qwen3-0.6B batch and 9% at 32 x 16,384 tokens).
+constexpr int kStreamWaves = 1024;
+constexpr int kMinPieceTokens = 256;  // shortest grab when the batch is small (128: the
+// 1 x 8,192 + 255 x 100 batch 5% slower; 512: 40% slower)
+// Grabs of fewer units than this keep two chunks of loads in flight (a
+// short grab is latency-bound); longer ones wait for each chunk's loads
+// before issuing the next (see drain_loads).
+constexpr int kDrainUnits = 16;
+
+// The grabs of one kv-head group: units [lo(j), lo(j + 1)) for grab j < W.
+struct Sched {
+  int C;  // units in all
+  int W;  // grabs (waves in use), at most C
+  __device__ __forceinline__ int lo(int j) const { return (int)((int64_t)j * C / W); }
+  // the grab holding unit x (< C)
+  __device__ __forceinline__ int grab_of(int x) const {
+    return (int)(((int64_t)(x + 1) * W - 1) / C);
+  }
+};
+
+template <int CHUNK>
+__device__ __forceinline__ int seq_units(const DecodeArgs& a, int s) {
+  const int n = min(clamp_len(seq_len(a, s), a.max_blocks, a.block_size), a.max_ctx);
+  return n <= 0 ? 1 : (n + CHUNK - 1) / CHUNK;
+}
+
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+template <int CHUNK>
+__device__ __forceinline__ int units_of(int n) {
+  return n <= 0 ? 1 : (n + CHUNK - 1) / CHUNK;
+}
+
+// Where grab j starts: the batch's schedule, the sequence b holding unit lo
+// (its first unit S and length n). Every length is read once (4 x 64 per
+// round, a wave-wide sum); the first 256 stay in registers for the search
+// (a wave-wide scan, then the first lane past lo), so a batch of up to 256
+// sequences costs one round trip. Wave-uniform: kept in scalar registers.
+struct GrabStart {
+  int b, S, n;
+};
+
+template <int CHUNK>
+__device__ __forceinline__ Sched stream_locate(const DecodeArgs& a, int slots, int j,
+                                               GrabStart& at) {
+  constexpr int KB = 4;
+  const int lane = threadIdx.x % kWave;
+  const int ns = a.num_seqs;
+  int keep[KB];  // lengths of sequences 64k + lane
+  int C = 0;
+  for (int base = 0; base < ns; base += KB * kWave) {
+    int n[KB], u = 0;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int s = base + k * kWave + lane;
+      n[k] = s < ns ? min(clamp_len(seq_len(a, s), a.max_blocks, a.block_size), a.max_ctx) : -1;
+      u += n[k] < 0 ? 0 : units_of<CHUNK>(n[k]);
+    }
+    if (base == 0) {
+#pragma unroll
+      for (int k = 0; k < KB; ++k) keep[k] = n[k];
+    }
+    C += wave_sum(u);
+  }
+  Sched sc;
+  sc.C = __builtin_amdgcn_readfirstlane(C);
+  sc.W = max(1, min(slots, sc.C / max(1, kMinPieceTokens / CHUNK)));
+  at.b = ns;
+  at.S = 0;
+  at.n = 0;
+  if (j >= sc.W) return sc;
+  const int x = sc.lo(j);
+  int S = 0;
+  for (int base = 0; base < ns; base += kWave) {
+    int n;
+    if (base < KB * kWave) {
+      const int k = base / kWave;
+      n = k == 0 ? keep[0] : k == 1 ? keep[1] : k == 2 ? keep[2] : keep[3];
+    } else {
+      const int s = base + lane;
+      n = s < ns ? min(clamp_len(seq_len(a, s), a.max_blocks, a.block_size), a.max_ctx) : -1;
+    }
+    const int u = n < 0 ? 0 : units_of<CHUNK>(n);
+    const int incl = wave_inclusive_scan(u, lane);
+    const uint64_t past = __ballot(S + incl > x);
+    if (past) {
+      const int l = __ffsll((long long)past) - 1;
+      at.b = __builtin_amdgcn_readfirstlane(base + l);
+      at.S = __builtin_amdgcn_readfirstlane(S + __shfl(incl - u, l, kWave));
+      at.n = __builtin_amdgcn_readfirstlane(__shfl(n, l, kWave));
+      return sc;
+    }
+    S = __builtin_amdgcn_readfirstlane(S + __shfl(incl, kWave - 1, kWave));
+  }
+  return sc;  // not reached: lo < C
+}
+
+template <int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1, bool MF = false>
+__global__ __launch_bounds__(kWave * VS) __attribute__((amdgpu_waves_per_eu(kSplitWavesPerSimd)))
+void decode_stream_kernel(DecodeArgs a, int slots) {
+  constexpr bool kPair = MF && VS > 1;
+  using L = Lanes<D, KPW>;
+  constexpr int CHUNK = L::TPI * (MF ? D / 16 : kVecUnroll);
+  // q-heads merged per wave, rounded up to a power of two
+  constexpr int HW = MF ? 16 : KPW * G;
+  constexpr int HP = (MF && G > 0 && G <= 8) ? 8 : HW;
+  const int Gn = G ? G : a.group;
+  const int H_kv = a.num_kv_heads;
+  const int H_q = H_kv * Gn;
+  const int n_groups = H_kv / (kPair ? VS : KPW);
+  const int gw = blockIdx.x % n_groups;
+  const int j = blockIdx.x / n_groups;  // this workgroup's grab
+  const int half = VS == 1 ? 0 : threadIdx.x / kWave;
+  // this wave's first kv-head and its q-heads
+  const int g0 = kPair ? gw * VS + half : gw * KPW * VS + half;
+  const int h0 = g0 * Gn;
+  const int nh = MF ? Gn : KPW * G;
+  char* lds_base = nullptr;
+  if constexpr (MF) {
+    __shared__ __attribute__((aligned(16))) char mf_lds[VS * mf_bytes(D)];
+    lds_base = mf_lds;
+  }
+
+  GrabStart at;
+  const Sched sc = stream_locate<CHUNK>(a, slots, j, at);
+  if (j >= sc.W) return;  // a small batch leaves some workgroups idle
+  const int lo = sc.lo(j), hi = sc.lo(j + 1);
+  const int lane = threadIdx.x % kWave;
+  const bool drain_on = sc.C / sc.W >= kDrainUnits;
+  // the sequence holding the current unit, its first unit and its length
+  int b = at.b, S = at.S, n_next = at.n;
+  const int b0 = b, S0 = S;
+  // Only a grab's first and last pieces can be part of a longer sequence,
+  // so a grab completes at most two sequences (bit 0: the first piece's,
+  // bit 1: the last piece's); they are merged after it, so the merge's
+  // registers stay out of the streaming loop.
+  int complete = 0;
+  int bl = b, Sl = S;  // the last piece's sequence and its first unit
+  for (int u = lo; u < hi && b < a.num_seqs; ++b) {
+    const int n = n_next;
+    const int c = units_of<CHUNK>(n);
+    const int u1 = min(hi, S + c);
+    // the next piece's length, read now so that it has arrived when needed
+    if (u1 < hi && b + 1 < a.num_seqs)
+      n_next = min(clamp_len(seq_len(a, b + 1), a.max_blocks, a.block_size), a.max_ctx);
+    const int first = sc.grab_of(S), last = sc.grab_of(S + c - 1);
+    const bool direct = first == last;
+    // the thread id, opaque to the compiler in each piece: what decode_piece
+    // derives from it (lane roles, load and LDS offsets) is computed in the
+    // piece, not hoisted out of this loop where it would hold registers
+    // across every piece's streaming loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    char* lds = MF ? lds_base + (VS == 1 ? 0 : tid / kWave) * mf_bytes(D) : nullptr;
+    decode_piece<D, G, KPW, FUSED, SMALL, DRAIN, VS, MF>(
+        a, lds, tid, b, n, (u - S) * CHUNK, min((u1 - S) * CHUNK, n), direct, (int64_t)j + b,
+        drain_on);
+    if (!direct) {
+      // publish the partial (its agent-scope stores complete), then count it
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      int before = 0;
+      if (lane == 0)
+        before = __hip_atomic_fetch_add(a.counters + (int64_t)b * H_kv + g0, 1,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__builtin_amdgcn_readfirstlane(before) == last - first)  // every other piece is in
+        complete |= u == lo ? 1 : 2;
+    }
+    bl = b;
+    Sl = S;
+    u = u1;
+    S += c;
+  }
+  for (int k = 0; k < 2; ++k) {
+    if (!(complete & (1 << k))) continue;
+    const int mb = k ? bl : b0;
+    const int ms = k ? Sl : S0;
+    const int first = sc.grab_of(ms), last = sc.grab_of(ms + seq_units<CHUNK>(a, mb) - 1);
+    merge_pieces<D, HP>(a, H_q, mb, h0, nh, (int64_t)first + mb, last - first + 1);
+    if (lane == 0)
+      __hip_atomic_store(a.counters + (int64_t)mb * H_kv + g0, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+using SplitFn = void (*)(DecodeArgs, int);
+
+// ST: the stream grid's kernel, else the partitioned grid's.
+template <bool ST, int D, int G, int KPW, bool FUSED, bool SMALL, bool DRAIN, int VS = 1,
+          bool MF = false>
+SplitFn kernel_of() {
+  if constexpr (ST) return decode_stream_kernel<D, G, KPW, FUSED, SMALL, DRAIN, VS, MF>;
+  else return decode_split_kernel<D, G, KPW, FUSED, SMALL, DRAIN, VS, MF>;
+}
 
 // DRAIN is built only where it changes the code: chunks of 8 loads (G < 8)
 // inside one block.
-template <int D, int KPW, bool FUSED, bool SMALL, bool DRAIN>
+template <bool ST, int D, int KPW, bool FUSED, bool SMALL, bool DRAIN>
 SplitFn pick_split(int G) {
   constexpr bool kD = DRAIN && !SMALL;
   switch (G) {
-    case 1: return decode_split_kernel<D, 1, KPW, FUSED, SMALL, kD>;
-    case 2: return decode_split_kernel<D, 2, KPW, FUSED, SMALL, kD>;
-    case 4: return decode_split_kernel<D, 4, KPW, FUSED, SMALL, kD>;
+    case 1: return kernel_of<ST, D, 1, KPW, FUSED, SMALL, kD>();
+    case 2: return kernel_of<ST, D, 2, KPW, FUSED, SMALL, kD>();
+    case 4: return kernel_of<ST, D, 4, KPW, FUSED, SMALL, kD>();
   }
   return nullptr;
 }
@@ -1130,42 +1438,43 @@ SplitFn pick_split(int G) {
 // The matrix-core variant (one kv-head per wave, VS waves per workgroup):
 // group sizes 8 and 16 built as such, the others (up to 16) take G from the
 // arguments.
-template <int D, bool FUSED, bool SMALL, bool DRAIN, int VS>
+template <bool ST, int D, bool FUSED, bool SMALL, bool DRAIN, int VS>
 SplitFn pick_split_mf(int G) {
   constexpr bool kD = DRAIN && !SMALL;
   switch (G) {
-    case 8: return decode_split_kernel<D, 8, 1, FUSED, SMALL, kD, VS, true>;
-    case 16: return decode_split_kernel<D, 16, 1, FUSED, SMALL, kD, VS, true>;
+    case 8: return kernel_of<ST, D, 8, 1, FUSED, SMALL, kD, VS, true>();
+    case 16: return kernel_of<ST, D, 16, 1, FUSED, SMALL, kD, VS, true>();
   }
-  return G >= 1 && G <= 16 ? decode_split_kernel<D, 0, 1, FUSED, SMALL, kD, VS, true> : nullptr;
+  return G >= 1 && G <= 16 ? kernel_of<ST, D, 0, 1, FUSED, SMALL, kD, VS, true>() : nullptr;
 }
 
-template <int D, bool FUSED, int VS>
+template <bool ST, int D, bool FUSED, int VS>
 SplitFn pick_split_mf(int G, bool small, bool drain) {
-  if (small) return pick_split_mf<D, FUSED, true, false, VS>(G);
-  return drain ? pick_split_mf<D, FUSED, false, true, VS>(G)
-               : pick_split_mf<D, FUSED, false, false, VS>(G);
+  if (small) return pick_split_mf<ST, D, FUSED, true, false, VS>(G);
+  return drain ? pick_split_mf<ST, D, FUSED, false, true, VS>(G)
+               : pick_split_mf<ST, D, FUSED, false, false, VS>(G);
 }
 
-template <int D, bool FUSED>
+template <bool ST, int D, bool FUSED>
 SplitFn pick_split_mf(int G, bool small, bool drain, int waves) {
   switch (waves) {
-    case 1: return pick_split_mf<D, FUSED, 1>(G, small, drain);
-    case 2: return pick_split_mf<D, FUSED, 2>(G, small, drain);
-    case 4: return pick_split_mf<D, FUSED, 4>(G, small, drain);
+    case 1: return pick_split_mf<ST, D, FUSED, 1>(G, small, drain);
+    case 2: return pick_split_mf<ST, D, FUSED, 2>(G, small, drain);
   }
   return nullptr;
 }
 
-template <int D, int KPW, bool FUSED>
+template <bool ST, int D, int KPW, bool FUSED>
 SplitFn pick_split(int G, bool small, bool drain) {
-  if (small) return pick_split<D, KPW, FUSED, true, false>(G);
-  return drain ? pick_split<D, KPW, FUSED, false, true>(G) : pick_split<D, KPW, FUSED, false, false>(G);
+  if (small) return pick_split<ST, D, KPW, FUSED, true, false>(G);
+  return drain ? pick_split<ST, D, KPW, FUSED, false, true>(G)
+               : pick_split<ST, D, KPW, FUSED, false, false>(G);
 }
 
-template <int D, int KPW>
+template <bool ST, int D, int KPW>
 SplitFn pick_split(int G, bool fused, bool small, bool drain) {
-  return fused ? pick_split<D, KPW, true>(G, small, drain) : pick_split<D, KPW, false>(G, small, drain);
+  return fused ? pick_split<ST, D, KPW, true>(G, small, drain)
+               : pick_split<ST, D, KPW, false>(G, small, drain);
 }
 
 constexpr int kSegmentBytes = 512;
@@ -1204,11 +1513,6 @@ int item_groups(const pa_desc* d) {
 }
 
 
-// Resident work items the split kernel keeps on an MI355X: 256 CUs x 8 waves.
-// A fixed constant (not a device query) so the workspace size is a pure
-// function of the arguments.
-constexpr int64_t kComputeUnits = 256;
-constexpr int64_t kResidentItems = kComputeUnits * 8;
 
 // Longest partition (16, 8, 4, 2 or 1 units of 256 tokens) whose wave count
 // still fills the chip, estimating the mean context as max_context_len / 2
@@ -1258,12 +1562,37 @@ bool ordered_grid(const pa_desc* d, int32_t num_seqs, int max_parts) {
          (int64_t)num_seqs * max_parts * item_groups(d) > kComputeUnits;
 }
 
+// Workspace layout, the same for every plan, so that one workspace serves
+// calls of any shape in turn: a fixed header of kMaxCounters words (the
+// stream grid's arrival counters, one per (sequence, kv-head); zero before
+// the first call, and every call leaves it zero), then the partials (o[d]
+// fp32, then (m, l) pairs), then, for the partitioned grid, the dispatch
+// order and the chosen partition length.
+constexpr int kMaxCounters = 1 << 16;  // (sequence, kv-head) pairs of a stream-grid call
+constexpr size_t kHeaderBytes = (size_t)kMaxCounters * sizeof(int32_t);
+
+// Tokens per chunk of the split kernels.
+int chunk_tokens(const pa_desc* d) {
+  if (use_mf(d)) return 32;
+  const int kpw = kv_heads_per_wave(d->head_dim, d->num_q_heads, d->num_kv_heads);
+  return (kWave / (d->head_dim / 8 * kpw)) * kVecUnroll;
+}
+
+// Grabs per kv-head group of the stream grid: its waves over the waves of
+// one grab (a matrix-core grab is a workgroup of VS waves).
+int stream_ranges(const pa_desc* d) {
+  return (int)max((int64_t)1, (int64_t)kStreamWaves / ((int64_t)item_groups(d) * kv_split(d)));
+}
+
 struct Plan {
+  bool stream;  // the stream grid (else the partitioned one)
+  int ranges;   // stream grid: ranges per kv-head group
   int part_tokens;
   int min_units;  // shortest partition the order kernel may choose, in 256 tokens
   int max_parts;
   bool ordered;
   bool auto_part;  // the partition length is the library's to choose
+  size_t partial_rows;  // partial rows (one per q-head each)
   size_t partial_bytes;
   size_t order_bytes;  // ranks, 16-byte rounded
   size_t ws_bytes;
@@ -1272,6 +1601,25 @@ struct Plan {
 Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part_blocks) {
   Plan p;
   p.auto_part = part_blocks <= 0;
+  // The stream grid needs a counter per (sequence, kv-head) and a unit count
+  // of the batch that fits an int.
+  const int64_t units = ((int64_t)max(1, max_ctx) + chunk_tokens(d) - 1) / chunk_tokens(d);
+  p.stream = p.auto_part && (int64_t)num_seqs * d->num_kv_heads <= kMaxCounters &&
+             (int64_t)num_seqs * units < ((int64_t)1 << 30);
+  if (p.stream) {
+    p.ranges = stream_ranges(d);
+    p.part_tokens = 0;
+    p.min_units = 0;
+    p.max_parts = 0;
+    p.ordered = false;
+    // row j + b for grab j < W
+    p.partial_rows = (size_t)p.ranges + max(1, num_seqs) - 1;
+    p.partial_bytes = p.partial_rows * d->num_q_heads * (size_t)(d->head_dim + 2) * sizeof(float);
+    p.order_bytes = 0;
+    p.ws_bytes = kHeaderBytes + p.partial_bytes;
+    return p;
+  }
+  p.ranges = 0;
   if (part_blocks <= 0) part_blocks = default_partition_blocks(d, num_seqs, max_ctx);
   // A partition at least as long as the longest context holds every
   // sequence whole, whatever its length: longer requests are cut to that.
@@ -1285,30 +1633,30 @@ Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part
     // the order kernel may cut down to a quarter of the estimate: room for
     // that many partitions (a grid 4x the items it fills measured no slower;
     // 16x cost 1.6% at the Qwen3-8B batch)
-    const int units = max(1, part_blocks / 4);
-    const int parts = max(1, (max_ctx + units * kPartUnit - 1) / (units * kPartUnit));
+    const int units4 = max(1, part_blocks / 4);
+    const int parts = max(1, (max_ctx + units4 * kPartUnit - 1) / (units4 * kPartUnit));
     if (ordered_grid(d, num_seqs, parts)) {
-      p.min_units = units;
+      p.min_units = units4;
       p.max_parts = parts;
     }
   }
-  p.partial_bytes = p.max_parts <= 1 ? 0
-                                     : (size_t)num_seqs * d->num_q_heads * p.max_parts *
-                                           (size_t)(d->head_dim + 2) * sizeof(float);
+  p.partial_rows = p.max_parts <= 1 ? 0 : (size_t)num_seqs * p.max_parts;  // row b * max_parts + p
+  p.partial_bytes = p.partial_rows * d->num_q_heads * (size_t)(d->head_dim + 2) * sizeof(float);
   const int64_t ranks = (int64_t)num_seqs * p.max_parts;
   p.ordered = ordered_grid(d, num_seqs, p.max_parts);
   p.order_bytes = p.ordered ? (size_t)((ranks * 4 + 15) & ~15) : 0;
   // then the partition length the order kernel chose (16 bytes)
-  p.ws_bytes = p.partial_bytes + p.order_bytes + (p.ordered ? 16 : 0);
+  const size_t body = p.partial_bytes + p.order_bytes + (p.ordered ? 16 : 0);
+  p.ws_bytes = body ? kHeaderBytes + body : 0;
   return p;
 }
 
 // Workspace in a library-owned device array, for callers that cannot
 // allocate (pa_decode_noalloc). Each GPU the library runs on holds its own
 // copy of the array until the process ends; every call on that GPU shares
-// it, so calls that overlap on one GPU race. The decode kernels write every
-// workspace byte they later read (dispatch order, chosen partition length,
-// partials), so nothing has to start at zero.
+// it, so calls that overlap on one GPU race. The array starts as zeros
+// (static storage), which is the state the counter header needs; every
+// call leaves the header zero, and writes every other byte it later reads.
 constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;  // per GPU
 constexpr int kMaxDevices = 64;
 
@@ -1402,7 +1750,8 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
       return fail(PA_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", who);
   }
   const int kpw = kv_heads_per_wave(desc->head_dim, desc->num_q_heads, desc->num_kv_heads);
-  const int64_t items = (int64_t)num_seqs * item_groups(desc) * plan.max_parts;
+  const int64_t items = plan.stream ? (int64_t)item_groups(desc) * plan.ranges
+                                    : (int64_t)num_seqs * item_groups(desc) * plan.max_parts;
   if (items > INT32_MAX) return fail(PA_ERR_INVALID_ARG, "%s: grid too large", who);
   if (debug_enabled()) {
     rc = debug_check_tables(who, block_tables, max_blocks_per_seq, context_lens, cu_k, num_seqs,
@@ -1410,6 +1759,8 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
     if (!rc && nt)
       rc = debug_check_slots(who, nt->slot_mapping, num_seqs,
                              desc->num_blocks * desc->block_size, (hipStream_t)stream);
+    if (!rc && plan.stream)
+      rc = debug_check_zero(who, workspace, kHeaderBytes, (hipStream_t)stream);
     if (rc) return rc;
   }
 
@@ -1420,9 +1771,10 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.cu_k = cu_k;
-  const size_t o_floats = (size_t)num_seqs * desc->num_q_heads * plan.max_parts * D;
-  a.ws_o = plan.ws_bytes ? (float*)workspace : nullptr;
-  a.ws_ml = plan.ws_bytes ? (float*)workspace + o_floats : nullptr;
+  const size_t o_floats = plan.partial_rows * desc->num_q_heads * D;
+  float* partials = plan.ws_bytes ? (float*)((char*)workspace + kHeaderBytes) : nullptr;
+  a.ws_o = partials;
+  a.ws_ml = partials ? partials + o_floats : nullptr;
   a.out = (uint16_t*)out;
   a.k_new = nt ? (const uint16_t*)nt->k : nullptr;
   a.v_new = nt ? (const uint16_t*)nt->v : nullptr;
@@ -1440,38 +1792,50 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.block_size = desc->block_size;
   a.block_shift = log2_int(desc->block_size);
   a.scale_log2 = scale * kLog2e;
-  a.order = plan.ordered ? (int32_t*)((char*)workspace + plan.partial_bytes) : nullptr;
-  a.part_dev = plan.ordered
-                   ? (int32_t*)((char*)workspace + plan.partial_bytes + plan.order_bytes)
-                   : nullptr;
+  char* after_partials = plan.ws_bytes ? (char*)workspace + kHeaderBytes + plan.partial_bytes
+                                       : nullptr;
+  a.order = plan.ordered ? (int32_t*)after_partials : nullptr;
+  a.part_dev = plan.ordered ? (int32_t*)(after_partials + plan.order_bytes) : nullptr;
   a.group = G;
+  a.max_ctx = max_context_len;
+  a.counters = plan.stream ? (int32_t*)workspace : nullptr;
 
   hipStream_t s = (hipStream_t)stream;
   const bool mf = use_mf(desc);
-  const int chunk = mf ? 32 : (kWave / (D / 8 * kpw)) * kVecUnroll;  // tokens per chunk
+  const int chunk = chunk_tokens(desc);
   const bool small = desc->block_size < chunk;
   const bool fused = nt != nullptr;
-  // the wave slots are full (2 per SIMD): one chunk of loads in flight per wave
-  const bool drain = items >= kResidentItems;
+  // the wave slots are full (2 per SIMD): one chunk of loads in flight per
+  // wave (the stream grid decides on the device, from the grab length)
+  const bool drain = plan.stream || items >= kResidentItems;
   SplitFn split = nullptr;
-  if (mf) {
-    const int waves = mf_waves(desc);
+  auto pick = [&](auto st) -> SplitFn {
+    constexpr bool ST = decltype(st)::value;
+    if (mf) {
+      const int waves = mf_waves(desc);
+      if (D == 128)
+        return fused ? pick_split_mf<ST, 128, true>(G, small, drain, waves)
+                     : pick_split_mf<ST, 128, false>(G, small, drain, waves);
+      return fused ? pick_split_mf<ST, 64, true>(G, small, drain, waves)
+                   : pick_split_mf<ST, 64, false>(G, small, drain, waves);
+    }
     if (D == 128)
-      split = fused ? pick_split_mf<128, true>(G, small, drain, waves)
-                    : pick_split_mf<128, false>(G, small, drain, waves);
-    else
-      split = fused ? pick_split_mf<64, true>(G, small, drain, waves)
-                    : pick_split_mf<64, false>(G, small, drain, waves);
-  } else if (D == 128) {
-    split = kpw == 2 ? pick_split<128, 2>(G, fused, small, drain)
-                     : pick_split<128, 1>(G, fused, small, drain);
-  } else {
-    split = kpw == 4   ? pick_split<64, 4>(G, fused, small, drain)
-            : kpw == 2 ? pick_split<64, 2>(G, fused, small, drain)
-                       : pick_split<64, 1>(G, fused, small, drain);
-  }
+      return kpw == 2 ? pick_split<ST, 128, 2>(G, fused, small, drain)
+                      : pick_split<ST, 128, 1>(G, fused, small, drain);
+    return kpw == 4   ? pick_split<ST, 64, 4>(G, fused, small, drain)
+           : kpw == 2 ? pick_split<ST, 64, 2>(G, fused, small, drain)
+                      : pick_split<ST, 64, 1>(G, fused, small, drain);
+  };
+  split = plan.stream ? pick(std::true_type{}) : pick(std::false_type{});
   if (!split || (D == 128 && kpw > 2))
     return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for %d kv-heads per wave", who, kpw);
+  if (plan.stream) {
+    // the vector path's workgroups (one wave) ask for a quarter of the LDS
+    // they do not use, so that four fit a CU: one wave per SIMD
+    hipLaunchKernelGGL(split, dim3((unsigned)items), dim3(kWave * kv_split(desc)), 0, s, a,
+                       plan.ranges);
+    return launch_status(who);
+  }
   if (plan.ordered) {
     const int round = (int)max((int64_t)1, kComputeUnits / item_groups(desc));
     PartRule rule = part_rule(desc);
@@ -1482,18 +1846,17 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
     rc = launch_status(who);
     if (rc) return rc;
   }
-  hipLaunchKernelGGL(split, dim3((unsigned)items), dim3(kWave * kv_split(desc)), 0, s, a);
+  hipLaunchKernelGGL(split, dim3((unsigned)items), dim3(kWave * kv_split(desc)), 0, s, a, 0);
   rc = launch_status(who);
   if (rc) return rc;
   if (plan.max_parts > 1) {
-    const unsigned wgs =
-        (unsigned)num_seqs * ((desc->num_q_heads + kReduceWaves - 1) / kReduceWaves);
+    const unsigned wgs = (unsigned)num_seqs * desc->num_q_heads;
     if (D == 128)
-      hipLaunchKernelGGL(decode_reduce_kernel<128>, dim3(wgs), dim3(kWave * kReduceWaves), 0, s,
-                         a, desc->num_q_heads);
+      hipLaunchKernelGGL(decode_reduce_kernel<128>, dim3(wgs), dim3(kWave), 0, s, a,
+                         desc->num_q_heads);
     else
-      hipLaunchKernelGGL(decode_reduce_kernel<64>, dim3(wgs), dim3(kWave * kReduceWaves), 0, s,
-                         a, desc->num_q_heads);
+      hipLaunchKernelGGL(decode_reduce_kernel<64>, dim3(wgs), dim3(kWave), 0, s, a,
+                         desc->num_q_heads);
     rc = launch_status(who);
     if (rc) return rc;
   }

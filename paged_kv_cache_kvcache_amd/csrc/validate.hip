@@ -24,6 +24,8 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <vector>
+
 #include "common.hpp"
 
 namespace pa {
@@ -235,6 +237,19 @@ int debug_check_varlen(const char* who, const int32_t* cu_q, const int32_t* cu_k
   hipLaunchKernelGGL(cu_kernel, dim3(grid_for(num_seqs)), dim3(kTile), 0, s, cu_q, cu_k,
                      num_seqs, max_seqlen_q, max_seqlen_k, decode_rows);
   return finish(who, s);
+}
+
+int debug_check_zero(const char* who, const void* p, size_t bytes, hipStream_t s) {
+  if (!bytes) return PA_OK;
+  std::vector<unsigned char> h(bytes);
+  if (hipMemcpyAsync(h.data(), p, bytes, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(PA_ERR_HIP, "%s: debug check: %s", who, hipGetErrorString(hipGetLastError()));
+  for (size_t i = 0; i < bytes; ++i)
+    if (h[i])
+      return fail(PA_ERR_WORKSPACE, "%s: debug check: workspace byte %zu of the counter header "
+                  "is not zero (zero the workspace before its first use)", who, i);
+  return PA_OK;
 }
 
 }  // namespace pa

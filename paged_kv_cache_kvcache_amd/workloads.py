@@ -259,7 +259,7 @@ def mixed_case(num_q_heads: int, num_kv_heads: int, head_dim: int, decode_lens, 
 # ------------------------------------------------------------ named workloads
 
 SEEDS = {"tiny": 1001, "qwen3-0.6b": 1002, "qwen3-8b": 1003, "long": 1004, "prefill": 1005,
-         "mixed": 1006, "gqa8": 1007, "gqa16": 1008}
+         "mixed": 1006, "gqa8": 1007, "gqa16": 1008, "skewed": 1009}
 
 DESCRIPTIONS = {
     "tiny": "decode, 4 q / 2 kv heads, d 64, B 256, pool 16, ctx {1,17,256,300}",
@@ -275,6 +275,9 @@ DESCRIPTIONS = {
     # qwen3-8b: 8 and 16 q-heads per kv-head
     "gqa8": "decode, 64 q / 8 kv heads, d 128, B 256, 256 seqs, ctx U[512,8192]",
     "gqa16": "decode, 64 q / 4 kv heads, d 128, B 256, 256 seqs, ctx U[512,8192]",
+    # one long context among short ones: the split-K partition and the grid's
+    # balance under the most uneven length mix of a decode batch
+    "skewed": "decode, 32 q / 8 kv heads, d 128, B 256, 256 seqs: 1 at ctx 8192 + 255 at 100",
 }
 
 
@@ -296,6 +299,8 @@ def make_case(name: str, seed: int | None = None, threads: int | None = None,
         return decode_case(32, 8, 128, ctx, seed + 1, **kw)
     if name == "long":
         return decode_case(32, 8, 128, [16384] * 32, seed + 1, **kw)
+    if name == "skewed":
+        return decode_case(32, 8, 128, [8192] + [100] * 255, seed + 1, **kw)
     if name in ("gqa8", "gqa16"):  # the qwen3-8b lengths, own contents
         ctx = np.random.default_rng(SEEDS["qwen3-8b"]).integers(512, 8192 + 1, size=256)
         return decode_case(64, 8 if name == "gqa8" else 4, 128, ctx, seed + 1, **kw)

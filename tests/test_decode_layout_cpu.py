@@ -183,3 +183,125 @@ def test_dispatch_order_is_a_permutation(seed):
         bulk, kb, kl = items[s]
         buckets.append(kb if j < bulk else kl)
     assert buckets == sorted(buckets, reverse=True)
+
+
+# ---- stream grid (decode_stream_kernel, stream_locate)
+
+def stream_schedule(units, slots, chunk, min_piece_tokens=256):
+    """stream_locate's schedule restated: units C, W equal grabs; lo(j) and
+    grab_of(x) as Sched computes them."""
+    C = int(sum(units))
+    W = max(1, min(slots, C // max(1, min_piece_tokens // chunk)))
+    return C, W, (lambda j: j * C // W), (lambda x: ((x + 1) * W - 1) // C)
+
+
+def find_sequence(units, x):
+    """stream_locate's search restated: 64 lengths per step, a scan, then
+    the first lane whose sequence ends past x."""
+    ns = len(units)
+    S = 0
+    for base in range(0, ns, 64):
+        u = np.zeros(64, dtype=np.int64)
+        m = min(64, ns - base)
+        u[:m] = units[base:base + m]
+        incl = np.cumsum(u)
+        past = np.nonzero(S + incl > x)[0]
+        if past.size:
+            l = int(past[0])
+            return base + l, S + int(incl[l] - u[l])
+        S += int(incl[-1])
+    raise AssertionError("x past the last unit")
+
+
+def stream_walk(lengths, slots, chunk):
+    """Every grab's pieces as its wave visits them: (grab, sequence, token
+    start, token end, direct, partial row, first, last)."""
+    units = [1 if n <= 0 else -(-n // chunk) for n in lengths]
+    C, W, lo, grab_of = stream_schedule(units, slots, chunk)
+    pieces = []
+    for j in range(W):
+        lo_j, hi_j = lo(j), lo(j + 1)
+        assert lo_j < hi_j, "an empty grab"
+        b, S = find_sequence(units, lo_j)
+        u = lo_j
+        while u < hi_j and b < len(lengths):
+            n, c = lengths[b], units[b]
+            u1 = min(hi_j, S + c)
+            first, last = grab_of(S), grab_of(S + c - 1)
+            pieces.append((j, b, (u - S) * chunk, min((u1 - S) * chunk, n), first == last,
+                           j + b, first, last))
+            u = u1
+            S += c
+            b += 1
+    return pieces, W, units
+
+
+@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_stream_grabs_cover_every_token_once(seed, chunk):
+    rng = np.random.default_rng(seed)
+    kind = seed % 5
+    ns = [1, 7, 64, 300, 700][kind]
+    if kind == 0:
+        lengths = [int(rng.integers(0, 40000))]
+    elif seed % 2:
+        lengths = [int(x) for x in rng.integers(0, 5000, size=ns)]
+    else:  # one long sequence among short ones, some empty rows
+        lengths = [int(x) for x in rng.integers(0, 120, size=ns)]
+        lengths[int(rng.integers(0, ns))] = 8192
+    slots = int(rng.choice([1, 3, 64, 256, 1024]))
+    pieces, W, units = stream_walk(lengths, slots, chunk)
+    covered = {}
+    rows = set()
+    per_seq = {}
+    for (j, b, s, e, direct, row, first, last) in pieces:
+        assert first <= j <= last < W
+        assert s % chunk == 0  # a piece starts on a chunk boundary
+        for t in range(s, e):
+            assert (b, t) not in covered, "token read twice"
+            covered[(b, t)] = j
+        per_seq.setdefault(b, []).append((j, direct, row, first, last))
+        if not direct:
+            assert row not in rows, "two pieces share a partial row"
+            rows.add(row)
+            assert 0 <= row < slots + len(lengths) - 1  # the workspace's rows
+    assert len(covered) == sum(lengths)
+    for b, n in enumerate(lengths):
+        ps = sorted(per_seq[b])
+        first, last = ps[0][3], ps[0][4]
+        assert [p[0] for p in ps] == list(range(first, last + 1))  # one piece per grab
+        assert all(p[1] == (first == last) for p in ps)
+        if n == 0:
+            assert len(ps) == 1 and ps[0][1]  # an empty row: one direct piece (its zeros)
+
+
+def test_stream_last_arriver_merges_once_in_any_arrival_order():
+    """The counter protocol: pieces of a split sequence arrive in any order;
+    exactly the arrival that sees count == pieces - 1 merges, and it leaves
+    the counter at zero; only a grab's first or last piece can complete a
+    sequence."""
+    rng = np.random.default_rng(5)
+    lengths = [int(x) for x in rng.integers(1, 9000, size=40)]
+    pieces, W, _ = stream_walk(lengths, 256, 16)
+    by_grab = {}
+    for p in pieces:
+        by_grab.setdefault(p[0], []).append(p)
+    for ps in by_grab.values():
+        for p in ps[1:-1]:
+            assert p[4], "a middle piece of a grab is a whole sequence"
+    split = {}
+    for p in pieces:
+        if not p[4]:
+            split.setdefault(p[1], []).append(p)
+    assert split
+    for b, ps in split.items():
+        for trial in range(5):
+            order = rng.permutation(len(ps))
+            cnt, merges = 0, 0
+            for i in order:
+                first, last = ps[i][6], ps[i][7]
+                before, cnt = cnt, cnt + 1
+                if before == last - first:
+                    merges += 1
+                    cnt = 0
+            assert merges == 1 and cnt == 0

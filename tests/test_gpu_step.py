@@ -131,7 +131,7 @@ def test_graph_replay_of_the_step_with_new_inputs(h_q):
     s_bt = dev_i32(tables)
     s_out = torch.empty_like(s_q)
     max_ctx = max_blocks * 256
-    ws = torch.empty(B.pa_decode_workspace_size(h_q, kc, bsz, max_ctx), dtype=torch.uint8,
+    ws = torch.zeros(B.pa_decode_workspace_size(h_q, kc, bsz, max_ctx), dtype=torch.uint8,
                      device="cuda")
 
     def step():

@@ -73,38 +73,50 @@ def test_host_argument_checks_need_no_gpu(lib):
     assert lib.pa_decode(None, None, None, None, 0, None, 0, 0, 1.0, None, None, 0,
                          ctypes.byref(d), None) == 0  # empty batch: no-op
     # workspace checked before any launch
-    # one partition of P blocks per work item: (m, l, o[d]) fp32 per
-    # (sequence, q-head, partition) when some sequence needs > 1 partition
+    # Every plan starts with a fixed 256 KiB header of arrival counters (one
+    # int32 per (sequence, kv-head) of a stream-grid call), then its partials.
+    HDR = 65536 * 4
+    # explicit partitions (the partitioned grid): one partial (o[d], m, l)
+    # fp32 per (sequence, q-head, partition) when some sequence needs > 1
+    # partition; nothing (not even the header) when none does
     for pb in (1, 2, 3):
         parts = -(-4096 // (256 * pb))
         assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4, 4096, pb) == \
-            4 * 32 * parts * (128 + 2) * 4
+            HDR + 4 * 32 * parts * (128 + 2) * 4
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4, 256, 1) == 0
-    assert lib.pa_decode_workspace_size(ctypes.byref(d), 4, 256) == 0
     # more work items (sequence x pair of kv-heads x partition) than the 256
     # CUs: the partials plus one int32 dispatch rank per (sequence,
     # partition), 16-byte rounded, and 16 bytes for the partition length the
     # order kernel chooses, up to 4096 sequences
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 256, 8192, 1) == \
-        256 * 32 * 32 * (128 + 2) * 4 + 256 * 32 * 4 + 16
-    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4096, 256, 1) == 4096 * 4 + 16
+        HDR + 256 * 32 * 32 * (128 + 2) * 4 + 256 * 32 * 4 + 16
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4096, 256, 1) == HDR + 4096 * 4 + 16
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 4097, 256, 1) == 0
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 64, 256, 1) == 0  # 256 items
-    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 65, 256, 1) == 65 * 4 + 12 + 16
-    # group size 8 at d 128 (matrix-core items of two kv-heads): the host
-    # estimates 4,096-token partitions once the waves (one per kv-head) fill a
-    # quarter of the 2,048 slots; with the dispatch order the workspace holds
-    # partitions down to a quarter of that (the order kernel may cut finer),
-    # so 64 sequences of up to 8,192 tokens take up to 8 partitions
-    g8 = _desc(h_q=64, h_kv=8)
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 65, 256, 1) == HDR + 65 * 4 + 12 + 16
+    # the library's choice (the stream grid): W grabs per kv-head group,
+    # W = 1,024 waves / (waves per grab x groups); one partial row per grab
+    # and sequence boundary, (W + num_seqs - 1) rows of H_q (o[d], m, l),
+    # whatever the context length
+    for ns, ctx in ((4, 256), (4, 4096), (256, 8192), (4096, 256)):
+        # 32 q / 8 kv heads, d 128: waves of two kv-heads, 4 groups -> W 256
+        assert lib.pa_decode_workspace_size(ctypes.byref(d), ns, ctx) == \
+            HDR + (256 + ns - 1) * 32 * (128 + 2) * 4
+    g8 = _desc(h_q=64, h_kv=8)  # matrix-core grabs: 2 waves, 4 groups -> W 128
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(g8), 64, 8192, 0) == \
-        64 * 64 * 8 * (128 + 2) * 4 + 64 * 8 * 4 + 16
-    # 32 sequences: 2,048-token estimate, up to 16 partitions of 512
-    assert lib.pa_decode_workspace_size_ex(ctypes.byref(g8), 32, 8192, 0) == \
-        32 * 64 * 16 * (128 + 2) * 4 + 32 * 16 * 4 + 16
+        HDR + (128 + 63) * 64 * (128 + 2) * 4
+    small = _desc(h_q=4, h_kv=2, d=64)  # one kv-head per wave: W 512
+    assert lib.pa_decode_workspace_size(ctypes.byref(small), 4, 300) == \
+        HDR + (512 + 3) * 4 * (64 + 2) * 4
+    # the header holds 65,536 (sequence, kv-head) counters: more pairs take
+    # the partitioned grid
+    assert lib.pa_decode_workspace_size(ctypes.byref(d), 8192, 256) == \
+        HDR + (256 + 8191) * 32 * (128 + 2) * 4
+    big = lib.pa_decode_workspace_size(ctypes.byref(d), 8193, 256)
+    assert big == 0  # 8,193 x 8 pairs: partitioned, one partition each, no ordering
     # an explicit partition length is kept: 2 partitions of 4,096
     assert lib.pa_decode_workspace_size_ex(ctypes.byref(g8), 64, 8192, 16) == \
-        64 * 64 * 2 * (128 + 2) * 4 + 64 * 2 * 4 + 16
+        HDR + 64 * 64 * 2 * (128 + 2) * 4 + 64 * 2 * 4 + 16
     need = lib.pa_decode_workspace_size(ctypes.byref(d), 4, 4096)
     assert need > 0
     fake = ctypes.c_void_p(0x1000)
@@ -218,7 +230,8 @@ def test_long_partitions_are_cut_to_the_longest_context(lib):
             whole = -(-ctx // 256)
             assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), seqs, ctx, pb) == \
                 lib.pa_decode_workspace_size_ex(ctypes.byref(d), seqs, ctx, min(pb, whole))
-    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 65, 8192, 200) == 65 * 4 + 12 + 16
+    assert lib.pa_decode_workspace_size_ex(ctypes.byref(d), 65, 8192, 200) == \
+        65536 * 4 + 65 * 4 + 12 + 16
     fake = ctypes.c_void_p(0x1000)
     assert lib.pa_decode(fake, fake, fake, fake, 2 ** 22 + 1, fake, 4, 2 ** 30 + 1, 0.125, fake,
                          None, 0, ctypes.byref(_desc(bsz=1024)), None) == B.PA_ERR_INVALID_ARG
@@ -231,13 +244,13 @@ def test_noalloc_refuses_batches_beyond_its_scratch_before_any_device_call(lib):
     after the usual argument checks."""
     d = _desc()
     fake = ctypes.c_void_p(0x1000)
-    need = lib.pa_decode_workspace_size(ctypes.byref(d), 2048, 16384)
+    need = lib.pa_decode_workspace_size(ctypes.byref(d), 4096, 16384)
     assert need > 64 << 20
-    assert lib.pa_decode_noalloc(fake, fake, fake, fake, 64, fake, 2048, 16384, 0.125, fake,
+    assert lib.pa_decode_noalloc(fake, fake, fake, fake, 64, fake, 4096, 16384, 0.125, fake,
                                  ctypes.byref(d), None) == B.PA_ERR_WORKSPACE
     msg = lib.pa_last_error().decode()
     assert "pa_decode_noalloc" in msg and str(need) in msg and str(64 << 20) in msg
-    assert lib.pa_decode_noalloc(fake, fake, fake, fake, 64, fake, 2048, 16384, -1.0, fake,
+    assert lib.pa_decode_noalloc(fake, fake, fake, fake, 64, fake, 4096, 16384, -1.0, fake,
                                  ctypes.byref(d), None) == B.PA_ERR_INVALID_ARG
     assert lib.pa_decode_noalloc(None, None, None, None, 0, None, 0, 0, 1.0, None,
                                  ctypes.byref(d), None) == 0  # empty batch: no-op
