@@ -469,9 +469,84 @@ def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
     if config == "qwen3-8b":
-        rec["tokens_per_s"]["model_36_layers"] = round(
+        rec["tokens_per_s"]["model_36_layers_from_one_layer"] = round(
             case.batch / (LAYERS_QWEN3_8B * ms_step * 1e-3), 1)
     return rec
+
+
+def run_model(args, torch, B, W, dev, layers: int = LAYERS_QWEN3_8B) -> dict:
+    """A whole decode step of the attention of a Qwen3-8B-shaped model: per
+    layer, the store of the batch's new tokens and decode over that layer's
+    own KV pool (36 pools of the Qwen3-8B batch, ~5.2 GB each, so no layer
+    is served from a cache filled by another), run four ways: eager or
+    replayed as one HIP graph, with pa_store_kv + pa_decode (separate) or
+    pa_decode_step (fused). The pools hold copies of one seeded pool (made
+    on the device); q and the new tokens are shared by the layers."""
+    case = W.make_case("qwen3-8b")
+    t, bf = _dev(torch, dev)
+    slots, _, _ = B.pa_build_metadata(case.block_tables, case.starts, case.context_lens,
+                                      case.block_size)
+    kc0, vc0 = bf(case.k_cache), bf(case.v_cache)
+    pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(layers - 1)]
+    q, k_new, v_new = bf(case.q), bf(case.k_new), bf(case.v_new)
+    out = torch.empty_like(q)
+    slots_d, bt_d, ctx_d = t(slots), t(case.block_tables), t(case.context_lens)
+    max_ctx = int(case.context_lens.max())
+    ws = torch.zeros(max(16, B.pa_decode_workspace_size(case.num_q_heads, kc0, case.batch,
+                                                        max_ctx)), dtype=torch.uint8, device=dev)
+
+    def separate():
+        for kc, vc in pools:
+            B.pa_store_kv(k_new, v_new, kc, vc, slots_d)
+            B.pa_decode(q, kc, vc, bt_d, ctx_d, case.scale, out, max_context_len=max_ctx,
+                        workspace=ws)
+
+    def fused():
+        for kc, vc in pools:
+            B.pa_decode_step(q, k_new, v_new, kc, vc, slots_d, bt_d, ctx_d, case.scale, out,
+                             max_context_len=max_ctx, workspace=ws)
+
+    def timed(run):
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / args.steps
+
+    def graphed(step):
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize(dev)
+        return g
+
+    ms = {"eager separate": timed(separate), "eager fused": timed(fused)}
+    g_sep, g_fused = graphed(separate), graphed(fused)
+    ms["graph separate"] = timed(g_sep.replay)
+    ms["graph fused"] = timed(g_fused.replay)
+    del g_sep, g_fused
+    db = decode_bytes(case) + store_bytes(case.batch, case.num_kv_heads, case.head_dim)
+    best = min(ms, key=ms.get)
+    return {
+        "workload": "%d layers x (%s); step = per layer, store of the batch's new tokens + "
+                    "decode over that layer's pool" % (layers, W.DESCRIPTIONS["qwen3-8b"]),
+        "layers": layers, "pool_gib_per_layer": round(2 * kc0.numel() * 2 / 2 ** 30, 2),
+        "ms_per_step": {k: round(v, 4) for k, v in ms.items()},
+        "tokens_per_s": {k: round(case.batch / (v * 1e-3), 1) for k, v in ms.items()},
+        "kv_gb_per_s": {k: round(layers * db / (v * 1e-3) / 1e9, 1) for k, v in ms.items()},
+        "best": best,
+    }
 
 
 # The other decode workloads and the prefill workload, timed by a default run
@@ -507,6 +582,9 @@ def main() -> int:
                     help="tokens per cache block (power of two, 16..1024); same lengths")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--model-only", action="store_true",
+                    help="time only the 36-layer decode step (eager and graph, separate and "
+                         "fused)")
     ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.cpu_baseline_child:
@@ -543,6 +621,9 @@ def main() -> int:
     def progress(msg):
         print("bench: " + msg, file=sys.stderr, flush=True)
 
+    if args.model_only:
+        print(json.dumps(run_model(args, torch, B, W, dev)), flush=True)
+        return 0
     if args.prefill_only:
         rec = run_prefill(args, torch, B, W, dev)
         rec["cpu_baseline"] = cpu_baseline(args, "prefill") if args.cpu_budget > 0 else None
@@ -582,6 +663,9 @@ def main() -> int:
             torch.cuda.empty_cache()
         progress("prefill")
         extra["prefill"] = run_prefill(args, torch, B, W, dev)
+        torch.cuda.empty_cache()
+        progress("36-layer step")
+        rec["model_36_layers"] = run_model(args, torch, B, W, dev)
         torch.cuda.empty_cache()
     if args.mixed:
         progress("mixed")

@@ -874,8 +874,11 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, char* lds, int
   const char* kc = reinterpret_cast<const char*>(a.k_cache);
   const char* vc = reinterpret_cast<const char*>(a.v_cache);
   // With the fused store the newest token (position n-1) is taken from
-  // k_new/v_new instead of the cache; only [start, cend) is read from the cache.
-  const int cend = (FUSED && end == n) ? n - 1 : end;
+  // k_new/v_new instead of the cache: full chunks cover only [start, cend),
+  // and the tail chunk, which then always exists, loads that token from the
+  // inputs in the same round of loads as its cache rows.
+  const bool has_new = FUSED && end == n;
+  const int cend = has_new ? n - 1 : end;
   const int nfull = (cend - start) / CHUNK;  // chunks with no token past cend
   // Full chunk i: its first token and the table entries of its blocks (one
   // when the chunk lies in one block, else one per load group of TPI
@@ -941,33 +944,38 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, char* lds, int
     }
   }
   const int c = start + nfull * CHUNK;
-  if (c < cend) {
+  if (c < end) {
     // tail: every lane finds its own token's row (clamped to the last valid
-    // token, which is masked out again in compute_chunk)
+    // token, which is masked out again in compute_chunk); the newest token's
+    // row comes from k_new/v_new
+    const char* kn = nullptr;
+    const char* vn = nullptr;
+    const int slot_new = has_new ? a.slot_mapping[b] : -1;  // read early, used last
+    if constexpr (FUSED) {
+      kn = reinterpret_cast<const char*>(a.k_new + (int64_t)b * a.k_new_stride + g * D + sub * 8);
+      vn = reinterpret_cast<const char*>(a.v_new + (int64_t)b * a.v_new_stride + g * D + sub * 8);
+    }
     uint4 kr[U], vr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = min(u * TPI + row, cend - 1 - c);
-      const int64_t off = token_offset(a, bt, c + t, row_bytes) + tail_lane_off;
-      kr[u] = load16(kc + off);
-      vr[u] = load16(vc + off);
+      const int t = min(u * TPI + row, end - 1 - c);
+      const bool fresh = has_new && c + t == n - 1;  // per lane: one load either way
+      const int64_t off = fresh ? 0 : token_offset(a, bt, c + t, row_bytes) + tail_lane_off;
+      kr[u] = load16(fresh ? kn : kc + off);
+      vr[u] = load16(fresh ? vn : vc + off);
     }
-    compute_chunk<L, D, G, U, true>(st, lds, a.scale_log2, lane, row, cend - c, kr, vr);
-  }
-  if (FUSED && end == n) {
-    // the newest token: attend to it from registers and write it to its slot
-    // (no work item of this call reads that cache row)
-    const uint4 kt = *reinterpret_cast<const uint4*>(a.k_new + (int64_t)b * a.k_new_stride + g * D + sub * 8);
-    const uint4 vt = *reinterpret_cast<const uint4*>(a.v_new + (int64_t)b * a.v_new_stride + g * D + sub * 8);
-    const uint4 kr1[1] = {kt};
-    const uint4 vr1[1] = {vt};
-    compute_chunk<L, D, G, 1, true>(st, lds, a.scale_log2, lane, row, 1, kr1, vr1);
-    const int slot_new = a.slot_mapping[b];
-    if (row == 0 && (kPair || half == 0) && slot_new >= 0 &&
-        slot_new < (a.num_blocks << a.block_shift)) {
-      const int64_t dst = (int64_t)slot_new * H_kv * D + g * D + sub * 8;
-      *reinterpret_cast<uint4*>(a.k_cache_w + dst) = kt;
-      *reinterpret_cast<uint4*>(a.v_cache_w + dst) = vt;
+    compute_chunk<L, D, G, U, true>(st, lds, a.scale_log2, lane, row, end - c, kr, vr);
+    if (has_new) {
+      // write the newest token to its slot (no piece of this call reads that
+      // cache row) from the lanes whose last load holds it: token e of the
+      // tail is load U-1 of row max(0, e - (U-1) * TPI)
+      const int e = end - 1 - c;
+      if (row == max(0, e - (U - 1) * TPI) && (kPair || half == 0) && slot_new >= 0 &&
+          slot_new < (a.num_blocks << a.block_shift)) {
+        const int64_t dst = (int64_t)slot_new * H_kv * D + g * D + sub * 8;
+        *reinterpret_cast<uint4*>(a.k_cache_w + dst) = kr[U - 1];
+        *reinterpret_cast<uint4*>(a.v_cache_w + dst) = vr[U - 1];
+      }
     }
   }
 

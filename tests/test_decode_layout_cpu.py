@@ -305,3 +305,21 @@ def test_stream_last_arriver_merges_once_in_any_arrival_order():
                     merges += 1
                     cnt = 0
             assert merges == 1 and cnt == 0
+
+
+@pytest.mark.parametrize("tpi,u_loads", [(2, 8), (4, 8), (8, 4), (1, 8), (4, 4)])
+def test_fused_store_lanes_hold_the_newest_token(tpi, u_loads):
+    """decode_piece's tail with the fused store: load u of lane row r reads
+    tail token min(u * TPI + r, e) (e = the newest token's index in the
+    tail), and the lanes of row max(0, e - (U-1) * TPI) write the newest
+    token from their last load: that load must hold token e, for every e
+    the tail can end on."""
+    chunk = tpi * u_loads
+    for e in range(chunk):
+        r = max(0, e - (u_loads - 1) * tpi)
+        assert 0 <= r < tpi
+        assert min((u_loads - 1) * tpi + r, e) == e
+        # and the newest token is the one the tail masks last: every load
+        # of a valid token index reads it at most once per row
+        seen = {min(u * tpi + row, e) for u in range(u_loads) for row in range(tpi)}
+        assert seen == set(range(e + 1))

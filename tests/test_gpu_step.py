@@ -180,3 +180,89 @@ def test_graph_replay_of_the_step_with_new_inputs(h_q):
         ref = oracle.decode(qn, cache_k, cache_v, tables, lens, 1 / np.sqrt(d))
         assert_close(got, ref, "replay %d" % it)
         assert np.all(got[~live] == 0)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_of_several_layers_shares_one_workspace(fused):
+    """Four layers, each with its own pool, captured as one graph (the
+    shape of a model's decode step: the layers' decode calls share one
+    workspace, whose arrival counters each call leaves at zero for the
+    next), replayed three times with new q and new tokens and eager work
+    between the replays. Every layer's output of every replay equals the
+    eager step's bit for bit, and the oracle's; the caches hold every
+    stored token. Lengths vary so that long sequences are split over
+    grabs and merged."""
+    rng = np.random.default_rng(321)
+    h_q, h_kv, d, layers = 32, 8, 128, 4
+    lens = np.array([3000, 1, 0, 777, 4096, 256, 2500, 90], dtype=np.int32)
+    bsz = len(lens)
+    max_blocks = 16
+    nb = bsz * max_blocks + 4
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = np.full((bsz, max_blocks), -1, dtype=np.int32)
+    for b in range(bsz):
+        tables[b] = perm[b * max_blocks:(b + 1) * max_blocks]
+    host = [(W.normal_bf16(rng, (nb, 256, h_kv, d)), W.normal_bf16(rng, (nb, 256, h_kv, d)))
+            for _ in range(layers)]
+    caches = [(dev_bf16(k), dev_bf16(v)) for k, v in host]
+    s_q = torch.zeros(bsz, h_q, d, dtype=torch.bfloat16, device="cuda")
+    s_k = torch.zeros(bsz, h_kv, d, dtype=torch.bfloat16, device="cuda")
+    s_v = torch.zeros(bsz, h_kv, d, dtype=torch.bfloat16, device="cuda")
+    live = lens > 0
+    slots = np.full(bsz, -1, dtype=np.int32)
+    slots[live] = B.pa_build_metadata(tables[live], np.maximum(lens - 1, 0)[live], lens[live],
+                                      256)[0]
+    s_slots, s_bt, s_ctx = dev_i32(slots), dev_i32(tables), dev_i32(lens)
+    outs = [torch.empty_like(s_q) for _ in range(layers)]
+    max_ctx = max_blocks * 256
+    ws = torch.zeros(B.pa_decode_workspace_size(h_q, caches[0][0], bsz, max_ctx),
+                     dtype=torch.uint8, device="cuda")
+    scale = 1 / np.sqrt(d)
+
+    def step(cs, os_):
+        for (kc, vc), out in zip(cs, os_):
+            if fused:
+                B.pa_decode_step(s_q, s_k, s_v, kc, vc, s_slots, s_bt, s_ctx, scale, out,
+                                 max_context_len=max_ctx, workspace=ws)
+            else:
+                B.pa_store_kv(s_k, s_v, kc, vc, s_slots)
+                B.pa_decode(s_q, kc, vc, s_bt, s_ctx, scale, out, max_context_len=max_ctx,
+                            workspace=ws)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        step(caches, outs)  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(caches, outs)
+    torch.cuda.synchronize()
+
+    ref_caches = [(k.copy(), v.copy()) for k, v in host]
+    for it in range(3):
+        qn = W.normal_bf16(rng, (bsz, h_q, d))
+        kn = W.normal_bf16(rng, (bsz, h_kv, d))
+        vn = W.normal_bf16(rng, (bsz, h_kv, d))
+        s_q.copy_(dev_bf16(qn))
+        s_k.copy_(dev_bf16(kn))
+        s_v.copy_(dev_bf16(vn))
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host_bits(o) for o in outs]
+        # eager work between replays: the same step on copies of the caches
+        eager_caches = [(kc.clone(), vc.clone()) for kc, vc in caches]
+        eager_outs = [torch.empty_like(s_q) for _ in range(layers)]
+        step(eager_caches, eager_outs)
+        torch.cuda.synchronize()
+        for l in range(layers):
+            assert np.array_equal(host_bits(eager_outs[l]), got[l]), \
+                "replay %d layer %d != eager" % (it, l)
+            ref_caches[l] = oracle.store_kv(ref_caches[l][0], ref_caches[l][1], kn, vn, slots)
+            assert np.array_equal(host_bits(caches[l][0]), ref_caches[l][0])
+            assert np.array_equal(host_bits(caches[l][1]), ref_caches[l][1])
+        for l in (0, layers - 1):
+            ref = oracle.decode(qn, ref_caches[l][0], ref_caches[l][1], tables, lens, scale)
+            assert_close(host_f64(outs[l]), ref, "replay %d layer %d" % (it, l))
+            assert np.all(host_f64(outs[l])[~live] == 0)
