@@ -1231,6 +1231,9 @@ constexpr int kMinPieceTokens = 256;  // shortest grab when the batch is small (
 // short grab is latency-bound); longer ones wait for each chunk's loads
 // before issuing the next (see drain_loads).
 constexpr int kDrainUnits = 16;
+// fixed cost of a piece, in units (0: the Qwen3-0.6B batch 2% slower, the
+// Qwen3-8B batch 1%; 4 and 8 no better)
+constexpr int kPieceCost = 2;
 
 // The grabs of one kv-head group: units [lo(j), lo(j + 1)) for grab j < W.
 struct Sched {
@@ -1269,6 +1272,17 @@ __device__ __forceinline__ int units_of(int n) {
   return n <= 0 ? 1 : (n + CHUNK - 1) / CHUNK;
 }
 
+// The cost of a sequence in the split: its units plus kPieceCost, the
+// fixed cost of starting a piece (its length, q and table reads and the
+// first loads, in units of streaming time), placed before its first unit.
+// Grabs of equal unit counts took up to 40% apart at the Qwen3-0.6B batch,
+// in the same order on every run: grabs holding more sequence starts were
+// the slow ones.
+template <int CHUNK>
+__device__ __forceinline__ int cost_of(int n) {
+  return units_of<CHUNK>(n) + kPieceCost;
+}
+
 // Where grab j starts: the batch's schedule, the sequence b holding unit lo
 // (its first unit S and length n). Every length is read once (4 x 64 per
 // round, a wave-wide sum); the first 256 stay in registers for the search
@@ -1292,7 +1306,7 @@ __device__ __forceinline__ Sched stream_locate(const DecodeArgs& a, int slots, i
     for (int k = 0; k < KB; ++k) {
       const int s = base + k * kWave + lane;
       n[k] = s < ns ? min(clamp_len(seq_len(a, s), a.max_blocks, a.block_size), a.max_ctx) : -1;
-      u += n[k] < 0 ? 0 : units_of<CHUNK>(n[k]);
+      u += n[k] < 0 ? 0 : cost_of<CHUNK>(n[k]);
     }
     if (base == 0) {
 #pragma unroll
@@ -1318,7 +1332,7 @@ __device__ __forceinline__ Sched stream_locate(const DecodeArgs& a, int slots, i
       const int s = base + lane;
       n = s < ns ? min(clamp_len(seq_len(a, s), a.max_blocks, a.block_size), a.max_ctx) : -1;
     }
-    const int u = n < 0 ? 0 : units_of<CHUNK>(n);
+    const int u = n < 0 ? 0 : cost_of<CHUNK>(n);
     const int incl = wave_inclusive_scan(u, lane);
     const uint64_t past = __ballot(S + incl > x);
     if (past) {
@@ -1365,54 +1379,59 @@ void decode_stream_kernel(DecodeArgs a, int slots) {
   const int lo = sc.lo(j), hi = sc.lo(j + 1);
   const int lane = threadIdx.x % kWave;
   const bool drain_on = sc.C / sc.W >= kDrainUnits;
-  // the sequence holding the current unit, its first unit and its length
+  // the sequence holding cost position u, where its cost starts, and its
+  // length; its units are cost positions [S + kPieceCost, S + kPieceCost + c)
   int b = at.b, S = at.S, n_next = at.n;
   const int b0 = b, S0 = S;
   // Only a grab's first and last pieces can be part of a longer sequence,
-  // so a grab completes at most two sequences (bit 0: the first piece's,
-  // bit 1: the last piece's); they are merged after it, so the merge's
+  // so a grab completes at most two sequences (bit 0: its first sequence's,
+  // bit 1: its last piece's); they are merged after it, so the merge's
   // registers stay out of the streaming loop.
   int complete = 0;
-  int bl = b, Sl = S;  // the last piece's sequence and its first unit
+  int bl = b, Sl = S;  // the last piece's sequence and where its cost starts
   for (int u = lo; u < hi && b < a.num_seqs; ++b) {
     const int n = n_next;
     const int c = units_of<CHUNK>(n);
-    const int u1 = min(hi, S + c);
+    const int f = S + kPieceCost;  // cost position of its first unit
+    const int u1 = min(hi, f + c);
     // the next piece's length, read now so that it has arrived when needed
     if (u1 < hi && b + 1 < a.num_seqs)
       n_next = min(clamp_len(seq_len(a, b + 1), a.max_blocks, a.block_size), a.max_ctx);
-    const int first = sc.grab_of(S), last = sc.grab_of(S + c - 1);
-    const bool direct = first == last;
-    // the thread id, opaque to the compiler in each piece: what decode_piece
-    // derives from it (lane roles, load and LDS offsets) is computed in the
-    // piece, not hoisted out of this loop where it would hold registers
-    // across every piece's streaming loop
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    char* lds = MF ? lds_base + (VS == 1 ? 0 : tid / kWave) * mf_bytes(D) : nullptr;
-    decode_piece<D, G, KPW, FUSED, SMALL, DRAIN, VS, MF>(
-        a, lds, tid, b, n, (u - S) * CHUNK, min((u1 - S) * CHUNK, n), direct, (int64_t)j + b,
-        drain_on);
-    if (!direct) {
-      // publish the partial (its agent-scope stores complete), then count it
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      int before = 0;
-      if (lane == 0)
-        before = __hip_atomic_fetch_add(a.counters + (int64_t)b * H_kv + g0, 1,
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__builtin_amdgcn_readfirstlane(before) == last - first)  // every other piece is in
-        complete |= u == lo ? 1 : 2;
+    const int p0 = max(u, f);  // this grab's units of the sequence: [p0, u1)
+    if (p0 < u1) {
+      const int first = sc.grab_of(f), last = sc.grab_of(f + c - 1);
+      const bool direct = first == last;
+      // the thread id, opaque to the compiler in each piece: what
+      // decode_piece derives from it (lane roles, load and LDS offsets) is
+      // computed in the piece, not hoisted out of this loop where it would
+      // hold registers across every piece's streaming loop
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      char* lds = MF ? lds_base + (VS == 1 ? 0 : tid / kWave) * mf_bytes(D) : nullptr;
+      decode_piece<D, G, KPW, FUSED, SMALL, DRAIN, VS, MF>(
+          a, lds, tid, b, n, (p0 - f) * CHUNK, min((u1 - f) * CHUNK, n), direct,
+          (int64_t)j + b, drain_on);
+      if (!direct) {
+        // publish the partial (its agent-scope stores complete), then count it
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        int before = 0;
+        if (lane == 0)
+          before = __hip_atomic_fetch_add(a.counters + (int64_t)b * H_kv + g0, 1,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__builtin_amdgcn_readfirstlane(before) == last - first)  // every other piece is in
+          complete |= b == b0 ? 1 : 2;
+      }
+      bl = b;
+      Sl = S;
     }
-    bl = b;
-    Sl = S;
     u = u1;
-    S += c;
+    S = f + c;
   }
   for (int k = 0; k < 2; ++k) {
     if (!(complete & (1 << k))) continue;
     const int mb = k ? bl : b0;
-    const int ms = k ? Sl : S0;
-    const int first = sc.grab_of(ms), last = sc.grab_of(ms + seq_units<CHUNK>(a, mb) - 1);
+    const int mf = (k ? Sl : S0) + kPieceCost;
+    const int first = sc.grab_of(mf), last = sc.grab_of(mf + seq_units<CHUNK>(a, mb) - 1);
     merge_pieces<D, HP>(a, H_q, mb, h0, nh, (int64_t)first + mb, last - first + 1);
     if (lane == 0)
       __hip_atomic_store(a.counters + (int64_t)mb * H_kv + g0, 0, __ATOMIC_RELAXED,
@@ -1611,7 +1630,8 @@ Plan make_plan(const pa_desc* d, int32_t num_seqs, int32_t max_ctx, int32_t part
   p.auto_part = part_blocks <= 0;
   // The stream grid needs a counter per (sequence, kv-head) and a unit count
   // of the batch that fits an int.
-  const int64_t units = ((int64_t)max(1, max_ctx) + chunk_tokens(d) - 1) / chunk_tokens(d);
+  const int64_t units = ((int64_t)max(1, max_ctx) + chunk_tokens(d) - 1) / chunk_tokens(d) +
+                        kPieceCost;
   p.stream = p.auto_part && (int64_t)num_seqs * d->num_kv_heads <= kMaxCounters &&
              (int64_t)num_seqs * units < ((int64_t)1 << 30);
   if (p.stream) {

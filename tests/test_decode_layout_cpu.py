@@ -213,25 +213,35 @@ def find_sequence(units, x):
     raise AssertionError("x past the last unit")
 
 
-def stream_walk(lengths, slots, chunk):
+PIECE_COST = 2  # kPieceCost: units of fixed cost placed before each sequence's units
+
+
+def stream_walk(lengths, slots, chunk, piece_cost=PIECE_COST):
     """Every grab's pieces as its wave visits them: (grab, sequence, token
-    start, token end, direct, partial row, first, last)."""
+    start, token end, direct, partial row, first, last). Grabs split the
+    batch's cost (each sequence: piece_cost, then its units); a grab's
+    piece of a sequence is its share of that sequence's units, none if the
+    grab holds only the sequence's fixed cost."""
     units = [1 if n <= 0 else -(-n // chunk) for n in lengths]
-    C, W, lo, grab_of = stream_schedule(units, slots, chunk)
+    cost = [u + piece_cost for u in units]
+    C, W, lo, grab_of = stream_schedule(cost, slots, chunk)
     pieces = []
     for j in range(W):
         lo_j, hi_j = lo(j), lo(j + 1)
         assert lo_j < hi_j, "an empty grab"
-        b, S = find_sequence(units, lo_j)
+        b, S = find_sequence(cost, lo_j)
         u = lo_j
         while u < hi_j and b < len(lengths):
             n, c = lengths[b], units[b]
-            u1 = min(hi_j, S + c)
-            first, last = grab_of(S), grab_of(S + c - 1)
-            pieces.append((j, b, (u - S) * chunk, min((u1 - S) * chunk, n), first == last,
-                           j + b, first, last))
+            f = S + piece_cost
+            u1 = min(hi_j, f + c)
+            p0 = max(u, f)
+            if p0 < u1:
+                first, last = grab_of(f), grab_of(f + c - 1)
+                pieces.append((j, b, (p0 - f) * chunk, min((u1 - f) * chunk, n),
+                               first == last, j + b, first, last))
             u = u1
-            S += c
+            S = f + c
             b += 1
     return pieces, W, units
 
