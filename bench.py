@@ -447,10 +447,12 @@ def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
     gbs = (db + sb) / (ms_step * 1e-3) / 1e9
     if mode == "fused":
         dom, dom_bytes = "pa_decode_step", db + sb
-        dom_desc = "pa_decode_step (order + store fused into split-K decode + merge)"
+        dom_desc = "pa_decode_step (decode_stream_kernel: one launch, split-K over balanced " \
+                   "grabs, merged in the kernel; the new tokens stored by it)"
     else:
         dom, dom_bytes = "pa_decode", db
-        dom_desc = "pa_decode (order + split-K + merge)"
+        dom_desc = "pa_decode (decode_stream_kernel: one launch, split-K over balanced grabs, " \
+                   "merged in the kernel)"
     dom_gbs = dom_bytes / (ms_call[dom] * 1e-3) / 1e9
     traffic = traffic_from_profile(pmc_decode_file(config), DECODE_SRC, mode, args.block_size,
                                    config)

@@ -44,10 +44,18 @@ def test_source_digest_ignores_comments(tmp_path):
 
 
 def test_committed_decode_records_name_their_workloads():
-    for config in ("qwen3-8b", "gqa8", "gqa16"):
+    """Every decode workload the default bench line reports (and the larger
+    GQA groups) has a counter record for the current decode source, so its
+    roofline carries measured traffic."""
+    for config in ("qwen3-8b", "qwen3-0.6b", "long", "skewed", "gqa8", "gqa16"):
         rec = json.load(open(bench.pmc_decode_file(config)))
         assert rec["config"] == config and rec["step_mode"] == "separate"
         assert rec["block_size"] == 256 and rec["traffic_bytes_per_launch"] > 0
+        assert rec["source_sha256_16"] == bench.src_hash(bench.DECODE_SRC), config
+    for path, src in ((bench.PMC_PREFILL_FILE, bench.PREFILL_SRC),
+                      (bench.PMC_STORE_FILE, bench.STORE_SRC)):
+        rec = json.load(open(path))
+        assert rec["source_sha256_16"] == bench.src_hash(src) and rec["traffic_bytes_per_launch"] > 0
 
 
 def test_more_than_one_gpu_is_refused_before_any_device_work():
