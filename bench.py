@@ -347,8 +347,8 @@ def run_mixed(args, torch, B, W, dev):
 def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
                graph: bool = False, replicas: int = 0) -> dict:
     """One decode workload: W untimed steps, then K steps back to back
-    between two events (the step time), then K steps again with events
-    around each call (per-call times; the roofline's). A step is
+    between two events (the step time), with an event after each call inside
+    that region (per-call times; the roofline's). A step is
     pa_store_kv of the batch's new tokens + pa_decode (mode "separate") or
     pa_decode_step (mode "fused"), optionally replayed as a HIP graph."""
     case = W.make_case(config, block_size=args.block_size)
@@ -417,28 +417,36 @@ def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
             run()
         torch.cuda.synchronize(dev)
 
-    # whole-step timing: K steps back to back between two events
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize(dev)
-    start.record()
-    for _ in range(args.steps):
-        run()
-    end.record()
-    torch.cuda.synchronize(dev)
-    ms_step = start.elapsed_time(end) / args.steps
-
-    # per-call durations: events around each call, on the launch stream
+    # K steps back to back, timed between two events; inside that region an
+    # event after each call gives the per-call durations (the roofline's).
+    # A replayed graph has no per-call events: its calls are timed in a
+    # second pass of eager steps.
     n = args.steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
           for _ in range(n)]
     torch.cuda.synchronize(dev)
+    start.record()
     for i in range(n):
+        if graph:
+            run()
+            continue
         pool = next_pool()
         ev[i][0].record()
         for j, (_, fn) in enumerate(calls):
             fn(pool)
             ev[i][j + 1].record()
+    end.record()
     torch.cuda.synchronize(dev)
+    ms_step = start.elapsed_time(end) / n
+    if graph:
+        for i in range(n):
+            pool = next_pool()
+            ev[i][0].record()
+            for j, (_, fn) in enumerate(calls):
+                fn(pool)
+                ev[i][j + 1].record()
+        torch.cuda.synchronize(dev)
     ms_call = {name: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / n
                for j, (name, _) in enumerate(calls)}
 
