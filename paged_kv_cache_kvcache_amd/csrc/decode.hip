@@ -87,6 +87,9 @@ struct DecodeArgs {
   int32_t* part_dev;
   int32_t group;   // q-heads per kv-head
   int32_t max_ctx;  // host bound of the lengths (the stream grid cuts longer ones there)
+  // layout of a partial's o[d] (see decode_piece): 0 = element order (the
+  // matrix-core path), else the lanes per head vector of the vector path
+  int32_t vec_lpt;
   int32_t* counters;  // stream grid: arrival count per (sequence, kv-head), zero between calls
   float scale_log2;
 };
@@ -1047,10 +1050,16 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, char* lds, int
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const int64_t wi = wrow + h;
+        // o[d] is stored pair-major (element pair k of lane group sub at
+        // 2 LPT k + 2 sub), so each store instruction writes LPT * 8
+        // contiguous bytes: element order would leave every 8-byte store 32
+        // bytes from its neighbour, and partial lines cost more to write
+        // through than their data
         if (row == 0) {
-          float* dst = a.ws_o + wi * D + sub * 8;
+          float* dst = a.ws_o + wi * D + sub * 2;
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) store_agent(dst + e, st.acc[h][e], st.acc[h][e + 1]);
+          for (int k = 0; k < 4; ++k)
+            store_agent(dst + 2 * LPT * k, st.acc[h][2 * k], st.acc[h][2 * k + 1]);
         }
         if (row == 0 && sub == 0) store_agent(a.ws_ml + wi * 2, st.m[h], st.l[h]);
       }
@@ -1065,13 +1074,21 @@ __device__ __forceinline__ void decode_piece(const DecodeArgs& a, char* lds, int
 // per head, each with D*HP/64 adjacent elements. The partials are read KP
 // at a time (one round of loads for up to that many) and folded into a
 // running max, so a merge of up to KP partials waits for memory once.
+// Where element d of a partial's o[] sits: element order, or pair-major for
+// the vector path (pair (d mod 8) / 2 of lane group d / 8 at 2 lpt pair +
+// 2 group; pairs (d, d + 1), d even, stay adjacent).
+__device__ __forceinline__ int partial_pos(int lpt, int d) {
+  return lpt ? ((d & 7) >> 1) * 2 * lpt + (d >> 3) * 2 + (d & 1) : d;
+}
+
 template <int D, int HP>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int H_q, int b, int h0, int nh,
                                              int64_t slot0, int np) {
   constexpr int LPH = kWave / HP;  // lanes per head
   constexpr int EPL = D / LPH;     // elements per lane
   static_assert(LPH >= 1 && EPL >= 1 && EPL <= 32, "merge geometry");
-  constexpr int KP = EPL >= 32 ? 1 : EPL >= 16 ? 2 : EPL >= 8 ? 4 : 8;
+  constexpr int KP = EPL >= 32 ? 4 : 8;  // up to 128 registers of partials per round (8 at a
+                                         // time: 32 x 16,384 tokens, 341 -> 336 us)
   const int lane = threadIdx.x % kWave;
   const int h = lane / LPH;
   if (h >= nh) return;
@@ -1088,16 +1105,17 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int H_q, int b
       const int p = min(p0 + k, np - 1);  // past the last: re-read it, weight 0 below
       const int64_t wi = (slot0 + p) * H_q + h0 + h;
       ml[k] = load_agent(a.ws_ml + wi * 2);
-      const float* s = a.ws_o + wi * D + e0;
+      const float* s = a.ws_o + wi * D;
       if constexpr (EPL % 2 == 0) {
 #pragma unroll
         for (int e = 0; e < EPL; e += 2) {
-          const float2 v = load_agent(s + e);
+          const float2 v = load_agent(s + partial_pos(a.vec_lpt, e0 + e));
           src[k][e] = v.x;
           src[k][e + 1] = v.y;
         }
       } else {
-        src[k][0] = __hip_atomic_load(s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        src[k][0] = __hip_atomic_load(s + partial_pos(a.vec_lpt, e0), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     float Mc = M;
@@ -1826,6 +1844,7 @@ int launch_decode(const char* who, const void* q, const void* k_cache, const voi
   a.part_dev = plan.ordered ? (int32_t*)(after_partials + plan.order_bytes) : nullptr;
   a.group = G;
   a.max_ctx = max_context_len;
+  a.vec_lpt = use_mf(desc) ? 0 : D / 8;
   a.counters = plan.stream ? (int32_t*)workspace : nullptr;
 
   hipStream_t s = (hipStream_t)stream;
