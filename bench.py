@@ -274,7 +274,7 @@ def run_prefill(args, torch, B, W, dev):
                         "pa_prefill_varlen": round(t_attn * 1e3, 5)},
         "q_tokens_per_s": round(n_q / (t_store + t_attn), 1),
         "algorithmic": {"prefill_flops": flops, "store_bytes": sb},
-        "roofline": {"bound": "mfma", "kernel": "pa_prefill_varlen (prefill_kernel)",
+        "roofline": {"bound": "mfma", "kernel": "pa_prefill_varlen (prefill32_kernel)",
                      "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic_from_profile(PMC_PREFILL_FILE, PREFILL_SRC, None)},

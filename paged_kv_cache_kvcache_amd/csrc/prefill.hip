@@ -8,26 +8,27 @@
 //
 // How (MI355X design):
 //   * Work item = workgroup of 8 waves for (sequence, kv-head, block of
-//     256/G query positions). Its 16 MFMA column tiles (two per wave) are 16
+//     256/G query positions). Its 16 column tiles (two per wave) are 16
 //     positions x 1 q-head each, covering all G q-heads of the kv-head, so
-//     every K/V tile staged in LDS serves the whole GQA group.
-//   * Scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_16x16x32_bf16: A = K rows from LDS, B = Q held in registers
-//     for the whole loop. The accumulator layout of S^T (one query column per
-//     lane, keys down the lane groups) is exactly the B-operand layout of the
-//     next product O^T += V^T P^T once the 32 keys of a step are numbered in
-//     the order the lanes hold them, so P never goes through LDS. V is staged
+//     every K/V stage staged in LDS serves the whole GQA group. A wave takes
+//     its two tiles as one 32-column tile of v_mfma_f32_32x32x16_bf16.
+//   * Scores are computed transposed, S^T = K Q^T: A = K rows from LDS, B =
+//     Q held in registers for the whole loop. The accumulator layout of S^T
+//     (one query column per lane pair, keys down the registers) is the
+//     B-operand layout of the next product O^T += V^T P^T once the keys of a
+//     16-key step are renumbered, so P never goes through LDS; V is staged
 //     transposed (d-major) in LDS in that key order.
 //   * Online softmax per query column: base-2 exponent with scale*log2(e)
-//     folded in, running max exchanged across the 4 lane groups of a column,
-//     P rounded to bf16 for the MFMA (the row sum adds the same rounded
-//     weights), fp32 accumulation, bf16 output.
+//     folded in, lazily rescaled running max, P rounded to bf16 for the MFMA
+//     (the row sum adds the same rounded weights), fp32 accumulation, bf16
+//     output.
 //   * Keys are staged 64 at a time (with blocks of 64 tokens or more a stage
-//     never straddles a block, so one block-table lookup per stage),
-//     double-buffered in LDS with register staging one stage ahead of LDS.
+//     never straddles a block, so one block-table lookup per stage), K one
+//     stage ahead of V in LDS so that each wave multiplies the next stage's
+//     scores while it runs the current stage's softmax; register staging
+//     brings each stage in a whole iteration before it is stored.
 //   * Causal work skipping: stages past the work item's last query are never
-//     loaded; a wave skips the stages that lie after all its queries; only
-//     stages that cross the diagonal apply the mask.
+//     loaded; only stages that cross the diagonal apply the mask.
 //   * Grid order: per sequence the last position blocks (the most keys) come
 //     first; consecutive workgroups differ in kv-head so one (sequence,
 //     kv-head)'s blocks, which re-read the same K/V, land on the same XCD.
@@ -39,7 +40,6 @@ namespace pa {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -47,7 +47,6 @@ constexpr int kWaves = 8;  // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
 constexpr int kNT = 2;     // 16-column tiles per wave
 constexpr int kTiles = kNT * kWaves;      // 16-column tiles per workgroup
-constexpr int kCols = 16 * kTiles;        // (position, q-head) columns per workgroup
 // Lazy rescaling: a column's reference max moves only when a score exceeds
 // it by more than 2^kLazyLog2 (weights stay <= 256, well inside bf16/fp32).
 constexpr float kLazyLog2 = 8.f;
@@ -94,12 +93,6 @@ template <> struct VVec<4> { typedef __attribute__((ext_vector_type(2))) unsigne
 template <> struct VVec<8> { typedef __attribute__((ext_vector_type(4))) unsigned int T; };
 template <> struct VVec<16> { typedef __attribute__((ext_vector_type(8))) unsigned int T; };
 
-// Position of key k (0..31) of a 32-key step in the order the MFMA lanes hold
-// it: lane group j holds keys 4j..4j+3 (first 16-key tile) then 16+4j..16+4j+3.
-__device__ __forceinline__ int key_slot(int k) {
-  return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
-}
-
 // acc + lo + hi of a packed bf16 pair, summed in fp32 (v_dot2_f32_bf16 with
 // the pair (1.0, 1.0)).
 __device__ __forceinline__ float sum_pair_bf16(uint32_t pair, float acc) {
@@ -115,78 +108,119 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// Row offset (in elements) of key position p of a sequence in a cache. A
-// broken table entry (precondition violated) reads block 0: the result is
-// then meaningless, but the access stays inside the pool.
-__device__ __forceinline__ int64_t key_row(const PrefillArgs& a, const int32_t* bt, int p,
-                                           int64_t row_elems) {
-  const int blk_raw = bt[p >> a.block_shift];
-  const int64_t blk = (blk_raw >= 0 && blk_raw < a.num_blocks) ? blk_raw : 0;
-  return ((blk << a.block_shift) + (p & (a.block_size - 1))) * row_elems;
+// ---- 32 x 32 tiles (v_mfma_f32_32x32x16_bf16), software-pipelined
+//
+// Each wave's two 16-column tiles are taken as one 32-column tile: column j
+// of a wave is column j % 16 of its tile j / 16. A 32 x 32 x 16 product
+// reads a 1 KiB A operand for 32 K FLOP, twice the work per LDS byte of a
+// 16 x 16 x 32 one. Lane layouts (checked on the GPU): A[i][k] in lane i + 32 (k / 8),
+// B[k][j] in lane j + 32 (k / 8), both 8 consecutive k; D[i][j] in lane
+// j + 32 h, register r, for i = 8 (r / 4) + 4 h + r % 4.
+//   * S^T = K Q^T per 32-key tile: A = 32 K rows from LDS, B = Q held in
+//     registers (8 d per lane per 16-d step).
+//   * Lane j + 32 h holds the scores of column j for keys 8q + 4h + c; its
+//     registers 8s .. 8s + 7 of a stage are the B operand of k-step s of
+//     O^T += V^T P^T when the 16 keys of a k-step are numbered with bits 2
+//     and 3 swapped: V^T is staged in that order (swap23), and P stays in
+//     registers.
+//   * A column's two lanes are the two halves of the wave: its max and sum
+//     are exchanged with v_permlane32_swap.
+//   * Pipelining: while the softmax of stage st runs on the vector ALU, the
+//     scores of stage st + 1 are already being multiplied, so each wave
+//     keeps the matrix unit fed on its own. K is therefore staged one stage
+//     ahead of V: at iteration st the LDS holds K of stage st + 1 and V of
+//     stage st, the registers bring in K of stage st + 3 and V of stage
+//     st + 2, and one barrier per stage guards both double buffers. The
+//     loop is unrolled twice so the two score arrays swap roles in place.
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+// Both lanes of a column (lanes c and c + 32) get max / sum of their values.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Register loads of stage `stage` (keys [64*stage, 64*stage + 64)). Keys at
-// or past kmax are never visible; they re-read the last needed one. SMALL:
-// blocks hold fewer keys than a stage, so every key looks up its own block;
-// otherwise the whole stage lies in one block (one lookup).
+// Physical block of the block holding key position p (a broken table entry
+// reads block 0: the result is then meaningless, but the access stays
+// inside the pool).
+__device__ __forceinline__ int64_t block_of(const PrefillArgs& a, const int32_t* bt, int p) {
+  const int raw = bt[p >> a.block_shift];
+  return (raw >= 0 && raw < a.num_blocks) ? raw : 0;
+}
+
+// Cache row of key position p: SMALL looks up p's own block, otherwise the
+// whole stage lies in the block `blk` (blocks hold at least a stage).
+template <bool SMALL>
+__device__ __forceinline__ int64_t cache_row(const PrefillArgs& a, const int32_t* bt, int64_t blk,
+                                             int p) {
+  if constexpr (SMALL) blk = block_of(a, bt, p);
+  return (blk << a.block_shift) + (p & (a.block_size - 1));
+}
+
+// Register loads of K (resp. V) of stage `stage`; keys at or past kmax are
+// never visible and re-read the last needed one.
 template <int D, bool SMALL>
-__device__ __forceinline__ void load_stage(const PrefillArgs& a, const int32_t* bt, int g, int kmax,
-                                           int stage, u32x4 (&kreg)[Geo<D>::KCHUNKS],
-                                           typename VVec<Geo<D>::VW>::T (&vreg)[2]) {
-  using GG = Geo<D>;
+__device__ __forceinline__ void load_k32(const PrefillArgs& a, const int32_t* bt, int64_t blk,
+                                         int g, int kmax, int stage,
+                                         u32x4 (&kreg)[Geo<D>::KCHUNKS]) {
   const int t = threadIdx.x;
-  const int kbase = stage * kKT;
   const int64_t row_elems = (int64_t)a.num_kv_heads * D;
   const uint16_t* kc = a.k_cache + (int64_t)g * D;
-  const uint16_t* vc = a.v_cache + (int64_t)g * D;
-  int64_t base = 0;
-  if constexpr (!SMALL) base = key_row(a, bt, kbase, row_elems) - (int64_t)kbase * row_elems;
-  // row offset of key position p (base + p rows when the stage is in one block)
-  auto row_of = [&](int p) -> int64_t {
-    if constexpr (SMALL) return key_row(a, bt, p, row_elems);
-    else return base + (int64_t)p * row_elems;
-  };
 #pragma unroll
-  for (int i = 0; i < GG::KCHUNKS; ++i) {
+  for (int i = 0; i < Geo<D>::KCHUNKS; ++i) {
     const int c = t + i * kThreads;
-    const int key = c / (D / 8);
-    const int ch = c % (D / 8);
-    const int kp = min(kbase + key, kmax - 1);
-    kreg[i] = *reinterpret_cast<const u32x4*>(kc + row_of(kp) + ch * 8);
+    const int kp = min(stage * kKT + c / (D / 8), kmax - 1);
+    kreg[i] = *reinterpret_cast<const u32x4*>(kc + cache_row<SMALL>(a, bt, blk, kp) * row_elems +
+                                              (c % (D / 8)) * 8);
   }
-  typedef typename VVec<GG::VW>::T VT;
-  const int pair = t % 32;  // keys 2*pair, 2*pair+1 of the stage
-  const int dg = t / 32;    // d range [dg*VW, dg*VW+VW)
+}
+
+template <int D, bool SMALL>
+__device__ __forceinline__ void load_v32(const PrefillArgs& a, const int32_t* bt, int64_t blk,
+                                         int g, int kmax, int stage,
+                                         typename VVec<Geo<D>::VW>::T (&vreg)[2]) {
+  typedef typename VVec<Geo<D>::VW>::T VT;
+  const int t = threadIdx.x;
+  const int64_t row_elems = (int64_t)a.num_kv_heads * D;
+  const uint16_t* vc = a.v_cache + (int64_t)g * D;
+  const int pair = t % 32;  // keys 2 pair, 2 pair + 1 of the stage
+  const int dg = t / 32;    // d range [dg VW, dg VW + VW)
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const int kp = min(kbase + 2 * pair + s, kmax - 1);
-    vreg[s] = *reinterpret_cast<const VT*>(vc + row_of(kp) + dg * GG::VW);
+    const int kp = min(stage * kKT + 2 * pair + s, kmax - 1);
+    vreg[s] = *reinterpret_cast<const VT*>(vc + cache_row<SMALL>(a, bt, blk, kp) * row_elems +
+                                           dg * Geo<D>::VW);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void store_stage(char* lds, const u32x4 (&kreg)[Geo<D>::KCHUNKS],
-                                            const typename VVec<Geo<D>::VW>::T (&vreg)[2]) {
-  using GG = Geo<D>;
+__device__ __forceinline__ void store_k32(char* kst, const u32x4 (&kreg)[Geo<D>::KCHUNKS]) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < GG::KCHUNKS; ++i) {
+  for (int i = 0; i < Geo<D>::KCHUNKS; ++i) {
     const int c = t + i * kThreads;
-    const int key = c / (D / 8);
-    const int ch = c % (D / 8);
-    *reinterpret_cast<u32x4*>(lds + key * GG::KROW + ch * 16) = kreg[i];
+    *reinterpret_cast<u32x4*>(kst + (c / (D / 8)) * Geo<D>::KROW + (c % (D / 8)) * 16) = kreg[i];
   }
-  // V^T[d][slot]: a dword holds the pair (V[2p][d], V[2p+1][d]); an even key
-  // and its odd neighbour occupy adjacent slots
-  const int pair = t % 32;
-  const int dg = t / 32;
-  const int key0 = 2 * pair;
-  const int slot = (key0 / 32) * 32 + key_slot(key0 % 32);
-  char* vt = lds + GG::KBYTES + slot * 2;
+}
+
+// V^T[d][slot]: a dword holds the pair (V[2p][d], V[2p+1][d]); swap23 keeps
+// an even key and its odd neighbour in adjacent slots
+template <int D>
+__device__ __forceinline__ void store_v32(char* vst, const typename VVec<Geo<D>::VW>::T (&vreg)[2]) {
+  using GG = Geo<D>;
+  const int t = threadIdx.x;
+  const int key0 = 2 * (t % 32);
+  const int slot = (key0 & ~15) + swap23(key0 & 15);
+  char* vt = vst + slot * 2;
 #pragma unroll
   for (int w = 0; w < GG::VW / 2; ++w) {
-    const int d = dg * GG::VW + 2 * w;
-    // element d: low halves; element d+1: high halves
+    const int d = (t / 32) * GG::VW + 2 * w;
     const uint32_t e0 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
     const uint32_t e1 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
     *reinterpret_cast<uint32_t*>(vt + d * GG::VROW) = e0;
@@ -194,25 +228,25 @@ __device__ __forceinline__ void store_stage(char* lds, const u32x4 (&kreg)[Geo<D
   }
 }
 
-// G_ = 0: the group size is taken from the arguments (any G up to kTiles).
 template <int D, int G_, bool SMALL>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void prefill32_kernel(PrefillArgs a) {
   using GG = Geo<D>;
+  typedef __attribute__((ext_vector_type(16))) float f32x16;
   const int G = G_ ? G_ : a.group;
   const int QB = positions_per_workgroup(G);  // query positions per workgroup
   const int used = (kTiles / G) * G;          // tiles with columns of their own
-  constexpr int KSTEPS = D / 32;             // MFMA k-steps over head_dim
-  constexpr int MT = D / 16;                 // 16-row tiles of O^T over head_dim
+  constexpr int KSTEPS = D / 16;              // 16-d steps of S^T
+  constexpr int DT = D / 32;                  // 32-row tiles of O^T over head_dim
+  // K buffers, then V^T buffers
   __shared__ __attribute__((aligned(16))) char lds[2 * GG::STAGE];
+  char* const kbuf = lds;
+  char* const vbuf = lds + 2 * GG::KBYTES;
 
   const int H_kv = a.num_kv_heads;
   const int H_q = H_kv * G;
   int idx = blockIdx.x;
   const int g = idx % H_kv;
   idx /= H_kv;
-  // A sequence's position blocks are consecutive (last positions first) and
-  // kv-head is fastest, so the blocks of one (sequence, kv-head), which read
-  // the same K/V, run together on one XCD and share its L2.
   const int r = idx % a.max_rblocks;  // position block counted from the end
   const int b = idx / a.max_rblocks;
 
@@ -231,188 +265,203 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
 
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
-  const int col = lane % 16;
-  const int grp = lane / 16;
+  const int j = lane % 32;  // this lane's column
+  const int h = lane / 32;  // which 8 of each 16 keys / d it holds
+  const int jt = j / 16;
 
   int head[kNT], pbase[kNT];
   bool own[kNT];  // a spare tile (when G does not divide kTiles) repeats a used one, unwritten
-  int wmax = -1;  // last position any column of this wave holds
 #pragma unroll
-  for (int j = 0; j < kNT; ++j) {
-    const int T = wave * kNT + j;
-    own[j] = T < used;
-    const int Tu = own[j] ? T : T - used;
-    head[j] = g * G + Tu % G;
-    pbase[j] = p0 + (Tu / G) * 16;
-    wmax = max(wmax, pbase[j] + 15);
+  for (int t2 = 0; t2 < kNT; ++t2) {
+    const int T = wave * kNT + t2;
+    own[t2] = T < used;
+    const int Tu = own[t2] ? T : T - used;
+    head[t2] = g * G + Tu % G;
+    pbase[t2] = p0 + (Tu / G) * 16;
   }
-  wmax = min(wmax, p_end - 1);
+  const int wmin = min(pbase[0], pbase[1]);  // first position any column holds
+  const int mypos = (jt ? pbase[1] : pbase[0]) + j % 16;
+  const int myhead = jt ? head[1] : head[0];
+  const bool myown = jt ? own[1] : own[0];
+  // First stage whose last key lies after the query of some column of the
+  // wave (wave-uniform, read into a scalar register for a scalar branch).
+  // From there on the mask runs, so a stage after all of the wave's queries
+  // (at most one: its positions span less than a stage) adds nothing.
+  const int diag_st = __builtin_amdgcn_readfirstlane(max(off + wmin + 1, 0) / kKT);
 
-  // Q^T operands for all k-steps (rows outside the sequence re-read row 0;
-  // their columns are never written)
-  bf16x8 qf[kNT][KSTEPS];
-#pragma unroll
-  for (int j = 0; j < kNT; ++j) {
-    const int pos = max(pbase[j] + col, 0);
-    const uint16_t* qp = a.q + ((int64_t)(q0 + pos) * H_q + head[j]) * D + grp * 8;
+  // Q^T operand for all 16-d steps (rows outside the sequence re-read row
+  // 0; their columns are never written)
+  bf16x8 qf[KSTEPS];
+  {
+    const uint16_t* qp = a.q + ((int64_t)(q0 + max(mypos, 0)) * H_q + myhead) * D + h * 8;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks)
-      qf[j][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 32));
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qp + ks * 16));
   }
 
-  f32x4 o[kNT][MT];
-  float m[kNT], l[kNT];
+  f32x16 o[DT];
+  float m = -INFINITY, l = 0.f;
 #pragma unroll
-  for (int j = 0; j < kNT; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.f;
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
-  // S^T = K Q^T for the 64 keys of the stage held in `kst` x (kNT x 16) columns
-  auto scores = [&](const char* kst, f32x4 (&sc)[kKT / 16][kNT]) {
+  // S^T of the two 32-key tiles of the K stage at `kst`
+  auto scores = [&](const char* kst, f32x16 (&sc)[2]) {
 #pragma unroll
-    for (int kt = 0; kt < kKT / 16; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int j = 0; j < kNT; ++j) sc[kt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const char* arow = kst + (kt * 16 + col) * GG::KROW + grp * 16;
+      for (int i = 0; i < 16; ++i) sc[kt][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const bf16x8 av =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(arow + ks * 64));
+    for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
-        for (int j = 0; j < kNT; ++j)
-          sc[kt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[j][ks], sc[kt][j], 0, 0, 0);
-      }
-    }
-  };
-  // Online softmax of the stage's scores per column, then O^T += V^T P^T
-  // with the stage's V^T held in `vst` (two 32-key products).
-  auto softmax_pv = [&](int key0, const f32x4 (&sc)[kKT / 16][kNT], const char* vst) {
-    // P^T operands for the two 32-key products (lane order of key_slot)
-    bf16x8 pf[kNT][kKT / 32];
-#pragma unroll
-    for (int j = 0; j < kNT; ++j) {
-      const int qpos = off + pbase[j] + col;  // absolute position of this column's query
-      float sv[kKT / 4];
-#pragma unroll
-      for (int kt = 0; kt < kKT / 16; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[kt * 4 + i] = sc[kt][j][i];
-      if (key0 + kKT - 1 > off + pbase[j]) {  // the stage crosses some column's diagonal
-#pragma unroll
-        for (int i = 0; i < kKT / 4; ++i) {
-          const int kpos = key0 + (i >> 2) * 16 + grp * 4 + (i & 3);
-          if (kpos > qpos) sv[i] = -INFINITY;
-        }
-      }
-      float mx = sv[0];
-#pragma unroll
-      for (int i = 1; i < kKT / 4; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, xor_lane(mx, 16));
-      mx = fmaxf(mx, xor_lane(mx, 32));
-      mx *= a.scale_log2;
-      // all lanes of a column see the same mx and m, so they agree on it
-      if (mx > m[j] + kLazyLog2) {
-        const float mnew = fmaxf(m[j], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m[j] - mnew);  // 0 on the first step
-        m[j] = mnew;
-        l[j] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) o[j][mt] *= alpha;
-      }
-      const float negm = (m[j] == -INFINITY) ? 0.f : -m[j];
-#pragma unroll
-      for (int h = 0; h < kKT / 32; ++h) {
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          p[i] = __builtin_amdgcn_exp2f(fmaf(sv[h * 8 + i], a.scale_log2, negm));
-        uint4 pk;
-        pk.x = pack2_bf16(p[0], p[1]);
-        pk.y = pack2_bf16(p[2], p[3]);
-        pk.z = pack2_bf16(p[4], p[5]);
-        pk.w = pack2_bf16(p[6], p[7]);
-        // the sum adds the rounded weights the MFMA sees (an exact weighted
-        // mean): a dot product of each packed pair with (1, 1)
-        l[j] = sum_pair_bf16(pk.x, l[j]);
-        l[j] = sum_pair_bf16(pk.y, l[j]);
-        l[j] = sum_pair_bf16(pk.z, l[j]);
-        l[j] = sum_pair_bf16(pk.w, l[j]);
-        pf[j][h] = __builtin_bit_cast(bf16x8, pk);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < kKT / 32; ++h) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const char* vrow = vst + (mt * 16 + col) * GG::VROW + (h * 32 + grp * 8) * 2;
-        const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vrow));
-#pragma unroll
-        for (int j = 0; j < kNT; ++j)
-          o[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf[j][h], o[j][mt], 0, 0, 0);
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 av = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(kst + (kt * 32 + j) * GG::KROW + ks * 32 +
+                                                    h * 16));
+        sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qf[ks], sc[kt], 0, 0, 0);
       }
     }
   };
 
-  // Register staging one stage ahead of LDS: at iteration st, stage st+1
-  // (loaded during the previous iteration) is copied into the LDS buffer of
-  // stage st-1, which every wave finished with before the last barrier, and
-  // stage st+2 is issued into the same registers, so its loads land while
-  // stage st is multiplied. Stage indices are clamped, so every issue is
-  // unconditional and the memory counter waits stay static.
+  // Register staging: kr holds K of stage st + 2, vr V of stage st + 1 when
+  // iteration st starts. Stage indices are clamped, so every load and store
+  // is unconditional: a buffer written past the last stage is never read.
   u32x4 kr[GG::KCHUNKS];
   typename VVec<GG::VW>::T vr[2];
-  load_stage<D, SMALL>(a, bt, g, kmax, 0, kr, vr);
-  store_stage<D>(lds, kr, vr);
-  load_stage<D, SMALL>(a, bt, g, kmax, min(1, n_stages - 1), kr, vr);
-  __syncthreads();
-  for (int st = 0; st < n_stages; ++st) {
-    if (st + 1 < n_stages) store_stage<D>(lds + ((st + 1) & 1) * GG::STAGE, kr, vr);
-    load_stage<D, SMALL>(a, bt, g, kmax, min(st + 2, n_stages - 1), kr, vr);
-    const char* ks_lds = lds + (st & 1) * GG::STAGE;
-    const int key0 = st * kKT;  // absolute position of the stage's first key
-    if (key0 <= off + wmax) {   // else every key is after every query of the wave
-      f32x4 s[kKT / 16][kNT];
-      scores(ks_lds, s);
-      softmax_pv(key0, s, ks_lds + GG::KBYTES);
+  int64_t blk_v = 0;  // block of the V stage loaded next (unused when SMALL)
+  auto staging = [&](int st) {
+    const int sk = min(st + 3, n_stages - 1);
+    const int64_t blk_k = SMALL ? 0 : block_of(a, bt, sk * kKT);
+    store_k32<D>(kbuf + (st & 1) * GG::KBYTES, kr);
+    store_v32<D>(vbuf + ((st + 1) & 1) * GG::VBYTES, vr);
+    load_k32<D, SMALL>(a, bt, blk_k, g, kmax, sk, kr);
+    load_v32<D, SMALL>(a, bt, blk_v, g, kmax, min(st + 2, n_stages - 1), vr);
+    blk_v = blk_k;
+  };
+
+  // One stage: softmax of `cur` (stage st), scores of stage st + 1 into
+  // `nxt`, O^T += V^T P^T of stage st. The next scores are computed even on
+  // the wave's last stage (the result is then never read): that keeps the
+  // stage one straight run of code the scheduler can interleave.
+  auto step = [&](int st, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    if (st >= diag_st) {  // the stage crosses some column's diagonal
+      // key 32 kt + 8 (r / 4) + 4 h + r % 4 of the stage at cur[kt][r]
+      const int thr = off + mypos - st * kKT - 4 * h;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int c = (i >> 4) * 32 + ((i & 15) >> 2) * 8 + (i & 3);
+        if (c > thr) cur[i >> 4][i & 15] = -INFINITY;
+      }
     }
+    float mx = cur[0][0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, cur[i >> 4][i & 15]);
+    mx = halves_max(mx) * a.scale_log2;
+    // both lanes of a column see the same mx and m, so they agree on it
+    const bool need = mx > m + kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mnew = need ? fmaxf(m, mx) : m;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;  // 0 on the first step
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
+    const float negm = (m == -INFINITY) ? 0.f : -m;
+    staging(st);
+    scores(kbuf + ((st + 1) & 1) * GG::KBYTES, nxt);
+    const char* vst = vbuf + (st & 1) * GG::VBYTES;
+#pragma unroll
+    for (int s = 0; s < kKT / 16; ++s) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        p[e] = __builtin_amdgcn_exp2f(fmaf(cur[s >> 1][(s & 1) * 8 + e], a.scale_log2, negm));
+      uint4 pk;
+      pk.x = pack2_bf16(p[0], p[1]);
+      pk.y = pack2_bf16(p[2], p[3]);
+      pk.z = pack2_bf16(p[4], p[5]);
+      pk.w = pack2_bf16(p[6], p[7]);
+      // the sum adds the rounded weights the MFMA sees (an exact weighted mean)
+      l = sum_pair_bf16(pk.x, l);
+      l = sum_pair_bf16(pk.y, l);
+      l = sum_pair_bf16(pk.z, l);
+      l = sum_pair_bf16(pk.w, l);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 av = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(vst + (dt * 32 + j) * GG::VROW +
+                                                    (s * 16 + h * 8) * 2));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf, o[dt], 0, 0, 0);
+      }
+    }
+  };
+  auto iterate = [&](int st, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    step(st, cur, nxt);
+    __syncthreads();
+  };
+
+  // Prologue: K and V of stage 0 to LDS, scores of stage 0, K of stage 1 to
+  // LDS; kr, vr then hold K of stage 2 and V of stage 1.
+  f32x16 sa[2], sb[2];
+  {
+    const int s1 = min(1, n_stages - 1), s2 = min(2, n_stages - 1);
+    const int64_t b0 = SMALL ? 0 : block_of(a, bt, 0);
+    const int64_t b1 = SMALL ? 0 : block_of(a, bt, s1 * kKT);
+    const int64_t b2 = SMALL ? 0 : block_of(a, bt, s2 * kKT);
+    load_k32<D, SMALL>(a, bt, b0, g, kmax, 0, kr);
+    load_v32<D, SMALL>(a, bt, b0, g, kmax, 0, vr);
+    store_k32<D>(kbuf, kr);
+    store_v32<D>(vbuf, vr);
+    load_k32<D, SMALL>(a, bt, b1, g, kmax, s1, kr);
+    load_v32<D, SMALL>(a, bt, b1, g, kmax, s1, vr);
+    __syncthreads();
+    scores(kbuf, sa);
+    store_k32<D>(kbuf + GG::KBYTES, kr);
+    load_k32<D, SMALL>(a, bt, b2, g, kmax, s2, kr);
+    blk_v = b2;
     __syncthreads();
   }
-
-  // ---- epilogue: column sums across the 4 lane groups, normalise, store
-#pragma unroll
-  for (int j = 0; j < kNT; ++j) {
-    float lt = l[j];
-    lt += xor_lane(lt, 16);
-    lt += xor_lane(lt, 32);
-    const int pos = pbase[j] + col;
-    if (!own[j] || pos < 0 || pos >= p_end) continue;
-    const float inv = 1.f / lt;
-    uint16_t* dst = a.out + ((int64_t)(q0 + pos) * H_q + head[j]) * D + grp * 4;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      uint2 v;
-      v.x = pack_bf16x2(o[j][mt][0] * inv, o[j][mt][1] * inv);
-      v.y = pack_bf16x2(o[j][mt][2] * inv, o[j][mt][3] * inv);
-      *reinterpret_cast<uint2*>(dst + mt * 16) = v;
-    }
+  for (int st = 0; st < n_stages; st += 2) {
+    iterate(st, sa, sb);
+    if (st + 1 < n_stages) iterate(st + 1, sb, sa);
   }
+
+  // ---- epilogue: column sum across the two lanes, normalise, store
+  const float lt = halves_sum(l);
+  if (!myown || mypos < 0 || mypos >= p_end) return;
+  const float inv = 1.f / lt;
+  uint16_t* dst = a.out + ((int64_t)(q0 + mypos) * H_q + myhead) * D + h * 4;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      uint2 v;
+      v.x = pack2_bf16(o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv);
+      v.y = pack2_bf16(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
+      *reinterpret_cast<uint2*>(dst + dt * 32 + q4 * 8) = v;
+    }
 }
 
 using PrefillFn = void (*)(PrefillArgs);
 
+template <int D, int G_, bool SMALL>
+PrefillFn kernel_for() {
+  return prefill32_kernel<D, G_, SMALL>;
+}
+
 template <int D, bool SMALL>
 PrefillFn pick(int G) {
   switch (G) {
-    case 1: return prefill_kernel<D, 1, SMALL>;
-    case 2: return prefill_kernel<D, 2, SMALL>;
-    case 4: return prefill_kernel<D, 4, SMALL>;
-    case 8: return prefill_kernel<D, 8, SMALL>;
-    case 16: return prefill_kernel<D, 16, SMALL>;
+    case 1: return kernel_for<D, 1, SMALL>();
+    case 2: return kernel_for<D, 2, SMALL>();
+    case 4: return kernel_for<D, 4, SMALL>();
+    case 8: return kernel_for<D, 8, SMALL>();
+    case 16: return kernel_for<D, 16, SMALL>();
   }
-  return G >= 1 && G <= kTiles ? prefill_kernel<D, 0, SMALL> : nullptr;  // other group sizes
+  return G >= 1 && G <= kTiles ? kernel_for<D, 0, SMALL>() : nullptr;  // other group sizes
 }
 
 }  // namespace
