@@ -324,20 +324,61 @@ __global__ __launch_bounds__(kThreads) void prefill32_kernel(PrefillArgs a) {
     }
   };
 
-  // Register staging: kr holds K of stage st + 2, vr V of stage st + 1 when
-  // iteration st starts. Stage indices are clamped, so every load and store
-  // is unconditional: a buffer written past the last stage is never read.
+  // ---- register staging: kr holds K of stage st + 2, vr V of stage st + 1
+  // when iteration st starts; the iteration stores them and brings in K of
+  // stage st + 3 and V of stage st + 2. Stage indices are clamped, so every
+  // load and store is unconditional: a buffer written past the last stage
+  // is never read. With blocks of at least a stage, the stage lies in one
+  // block, so a load is a scalar base plus a per-thread offset fixed for the
+  // whole loop, and the block's table entry is read an iteration ahead. K
+  // rows past kmax are read as they are (same block, and the mask removes
+  // their scores); V rows past kmax re-read row kmax - 1, since a zero
+  // weight times a non-finite stale value would not vanish. Smaller blocks
+  // look every key up on its own (load_k32 / load_v32).
+  typedef typename VVec<GG::VW>::T VT;
+  const int row_e = H_kv * D;           // elements per cache row
+  const int pair = threadIdx.x % 32;    // V: keys 2 pair, 2 pair + 1 of a stage
+  const int dg = threadIdx.x / 32;      // V: d range [dg VW, dg VW + VW)
+  uint32_t koff[GG::KCHUNKS], voff[2];  // element offsets from a stage's first row
+#pragma unroll
+  for (int i = 0; i < GG::KCHUNKS; ++i) {
+    const int c = threadIdx.x + i * kThreads;
+    koff[i] = (uint32_t)((c / (D / 8)) * row_e + (c % (D / 8)) * 8);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) voff[s] = (uint32_t)((2 * pair + s) * row_e + dg * GG::VW);
   u32x4 kr[GG::KCHUNKS];
-  typename VVec<GG::VW>::T vr[2];
-  int64_t blk_v = 0;  // block of the V stage loaded next (unused when SMALL)
+  VT vr[2];
+  // K of stage sk (in block bk) and V of stage sv (in block bv)
+  auto load_kv = [&](int sk, int64_t bk, int sv, int64_t bv) {
+    if constexpr (SMALL) {
+      load_k32<D, true>(a, bt, 0, g, kmax, sk, kr);
+      load_v32<D, true>(a, bt, 0, g, kmax, sv, vr);
+    } else {
+      const int kb = sk * kKT, vb = sv * kKT;
+      const uint16_t* kp =
+          a.k_cache + ((bk << a.block_shift) + (kb & (a.block_size - 1))) * row_e + g * D;
+      const uint16_t* vp =
+          a.v_cache + ((bv << a.block_shift) + (vb & (a.block_size - 1))) * row_e + g * D;
+#pragma unroll
+      for (int i = 0; i < GG::KCHUNKS; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kp + koff[i]);
+      const uint32_t vlast = (uint32_t)((kmax - 1 - vb) * row_e + dg * GG::VW);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        vr[s] = *reinterpret_cast<const VT*>(vp + (vb + 2 * pair + s < kmax ? voff[s] : vlast));
+    }
+  };
+  int64_t bk = 0, bv = 0;  // blocks of the iteration's K and V loads
+  int raw_next = 0;        // table entry of the next iteration's K block
   auto staging = [&](int st) {
-    const int sk = min(st + 3, n_stages - 1);
-    const int64_t blk_k = SMALL ? 0 : block_of(a, bt, sk * kKT);
+    const int64_t bk_now =
+        SMALL ? 0 : ((raw_next >= 0 && raw_next < a.num_blocks) ? raw_next : 0);
+    if constexpr (!SMALL) raw_next = bt[(min(st + 4, n_stages - 1) * kKT) >> a.block_shift];
+    bv = bk;
+    bk = bk_now;
     store_k32<D>(kbuf + (st & 1) * GG::KBYTES, kr);
     store_v32<D>(vbuf + ((st + 1) & 1) * GG::VBYTES, vr);
-    load_k32<D, SMALL>(a, bt, blk_k, g, kmax, sk, kr);
-    load_v32<D, SMALL>(a, bt, blk_v, g, kmax, min(st + 2, n_stages - 1), vr);
-    blk_v = blk_k;
+    load_kv(min(st + 3, n_stages - 1), bk, min(st + 2, n_stages - 1), bv);
   };
 
   // One stage: softmax of `cur` (stage st), scores of stage st + 1 into
@@ -346,6 +387,8 @@ __global__ __launch_bounds__(kThreads) void prefill32_kernel(PrefillArgs a) {
   // stage one straight run of code the scheduler can interleave.
   auto step = [&](int st, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     if (st >= diag_st) {  // the stage crosses some column's diagonal
+      // (kept a branch: the mask is not worth running on every stage)
+      asm volatile("" ::: "memory");
       // key 32 kt + 8 (r / 4) + 4 h + r % 4 of the stage at cur[kt][r]
       const int thr = off + mypos - st * kKT - 4 * h;
 #pragma unroll
@@ -407,21 +450,20 @@ __global__ __launch_bounds__(kThreads) void prefill32_kernel(PrefillArgs a) {
   // LDS; kr, vr then hold K of stage 2 and V of stage 1.
   f32x16 sa[2], sb[2];
   {
-    const int s1 = min(1, n_stages - 1), s2 = min(2, n_stages - 1);
+    const int s1 = min(1, n_stages - 1), s2 = min(2, n_stages - 1), s3 = min(3, n_stages - 1);
     const int64_t b0 = SMALL ? 0 : block_of(a, bt, 0);
     const int64_t b1 = SMALL ? 0 : block_of(a, bt, s1 * kKT);
     const int64_t b2 = SMALL ? 0 : block_of(a, bt, s2 * kKT);
-    load_k32<D, SMALL>(a, bt, b0, g, kmax, 0, kr);
-    load_v32<D, SMALL>(a, bt, b0, g, kmax, 0, vr);
+    load_kv(0, b0, 0, b0);
     store_k32<D>(kbuf, kr);
     store_v32<D>(vbuf, vr);
-    load_k32<D, SMALL>(a, bt, b1, g, kmax, s1, kr);
-    load_v32<D, SMALL>(a, bt, b1, g, kmax, s1, vr);
+    load_kv(s1, b1, s1, b1);
     __syncthreads();
     scores(kbuf, sa);
     store_k32<D>(kbuf + GG::KBYTES, kr);
-    load_k32<D, SMALL>(a, bt, b2, g, kmax, s2, kr);
-    blk_v = b2;
+    load_kv(s2, b2, s1, b1);  // vr: V of stage 1 again
+    bk = b2;                  // iteration 0 loads V of stage 2 from it
+    if constexpr (!SMALL) raw_next = bt[(s3 * kKT) >> a.block_shift];
     __syncthreads();
   }
   for (int st = 0; st < n_stages; st += 2) {
