@@ -222,7 +222,7 @@ def _dev(torch, dev):
     return t, bf
 
 
-def run_prefill(args, torch, B, W, dev):
+def run_prefill(args, torch, B, W, dev, warmup=None):
     """The prefix-cached prefill workload: pa_store_kv of the 18,342 new
     tokens, then pa_prefill_varlen. Two rooflines: the prefill kernel
     (causal-exact FLOPs, dense bf16 MFMA peak) and the store (bytes, HBM)."""
@@ -243,7 +243,7 @@ def run_prefill(args, torch, B, W, dev):
     def attn():
         B.pa_prefill_varlen(q, kc, vc, cuq_d, cuk_d, mq, mk, bt_d, case.scale, out)
 
-    for _ in range(max(1, args.warmup)):
+    for _ in range(max(1, args.warmup if warmup is None else warmup)):
         store()
         attn()
     torch.cuda.synchronize(dev)
@@ -345,7 +345,7 @@ def run_mixed(args, torch, B, W, dev):
 
 
 def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
-               graph: bool = False, replicas: int = 0) -> dict:
+               graph: bool = False, replicas: int = 0, warmup=None) -> dict:
     """One decode workload: W untimed steps, then K steps back to back
     between two events (the step time), with an event after each call inside
     that region (per-call times; the roofline's). A step is
@@ -397,7 +397,9 @@ def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
         for _, fn in calls:
             fn(pool)
 
-    for _ in range(args.warmup):
+    if warmup is None:
+        warmup = args.warmup
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize(dev)
     run = step
@@ -413,7 +415,7 @@ def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
             step()
         torch.cuda.synchronize(dev)
         run = g.replay
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             run()
         torch.cuda.synchronize(dev)
 
@@ -562,6 +564,10 @@ def run_model(args, torch, B, W, dev, layers: int = LAYERS_QWEN3_8B) -> dict:
 # The other decode workloads and the prefill workload, timed by a default run
 # beside the Qwen3-8B headline (each with its own roofline and CPU baseline).
 EXTRA_DECODE = ("qwen3-0.6b", "long", "skewed")
+# Untimed warm-up calls, at least, before each of the extra workloads of the
+# default line (the headline step takes exactly --warmup): after only 5, the
+# prefill workload measured about 10% slower than after 20 on the same GPU.
+EXTRA_WARMUP = 10
 
 
 def main() -> int:
@@ -669,10 +675,12 @@ def main() -> int:
             if config == args.config:
                 continue
             progress("%s decode" % config)
-            extra[config] = run_decode(args, torch, B, W, dev, config)
+            extra[config] = run_decode(args, torch, B, W, dev, config,
+                                       warmup=max(args.warmup, EXTRA_WARMUP))
             torch.cuda.empty_cache()
         progress("prefill")
-        extra["prefill"] = run_prefill(args, torch, B, W, dev)
+        extra["prefill"] = run_prefill(args, torch, B, W, dev,
+                                       warmup=max(args.warmup, EXTRA_WARMUP))
         torch.cuda.empty_cache()
         progress("36-layer step")
         rec["model_36_layers"] = run_model(args, torch, B, W, dev)
