@@ -362,7 +362,9 @@ __global__ __launch_bounds__(kThreads) void prefill32_kernel(PrefillArgs a) {
           a.v_cache + ((bv << a.block_shift) + (vb & (a.block_size - 1))) * row_e + g * D;
 #pragma unroll
       for (int i = 0; i < GG::KCHUNKS; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kp + koff[i]);
-      const uint32_t vlast = (uint32_t)((kmax - 1 - vb) * row_e + dg * GG::VW);
+      // (selected only on the last stage, where kmax - 1 - vb < 64; clamped so
+      // the product stays in range on the others)
+      const uint32_t vlast = (uint32_t)(min(kmax - 1 - vb, kKT - 1) * row_e + dg * GG::VW);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         vr[s] = *reinterpret_cast<const VT*>(vp + (vb + 2 * pair + s < kmax ? voff[s] : vlast));
