@@ -222,7 +222,7 @@ def _dev(torch, dev):
     return t, bf
 
 
-def run_prefill(args, torch, B, W, dev, warmup=None):
+def run_prefill(args, torch, B, W, dev, warmup=None, warm_s=0.0):
     """The prefix-cached prefill workload: pa_store_kv of the 18,342 new
     tokens, then pa_prefill_varlen. Two rooflines: the prefill kernel
     (causal-exact FLOPs, dense bf16 MFMA peak) and the store (bytes, HBM)."""
@@ -243,10 +243,11 @@ def run_prefill(args, torch, B, W, dev, warmup=None):
     def attn():
         B.pa_prefill_varlen(q, kc, vc, cuq_d, cuk_d, mq, mk, bt_d, case.scale, out)
 
-    for _ in range(max(1, args.warmup if warmup is None else warmup)):
+    def both():
         store()
         attn()
-    torch.cuda.synchronize(dev)
+
+    warm(torch, dev, both, max(1, args.warmup if warmup is None else warmup), warm_s)
     n = max(3, args.steps)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
     for i in range(n):
@@ -345,7 +346,7 @@ def run_mixed(args, torch, B, W, dev):
 
 
 def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
-               graph: bool = False, replicas: int = 0, warmup=None) -> dict:
+               graph: bool = False, replicas: int = 0, warmup=None, warm_s=0.0) -> dict:
     """One decode workload: W untimed steps, then K steps back to back
     between two events (the step time), with an event after each call inside
     that region (per-call times; the roofline's). A step is
@@ -399,9 +400,7 @@ def run_decode(args, torch, B, W, dev, config: str, mode: str = "separate",
 
     if warmup is None:
         warmup = args.warmup
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize(dev)
+    warm(torch, dev, step, warmup, warm_s)
     run = step
     if graph:
         side = torch.cuda.Stream(device=dev)
@@ -564,10 +563,26 @@ def run_model(args, torch, B, W, dev, layers: int = LAYERS_QWEN3_8B) -> dict:
 # The other decode workloads and the prefill workload, timed by a default run
 # beside the Qwen3-8B headline (each with its own roofline and CPU baseline).
 EXTRA_DECODE = ("qwen3-0.6b", "long", "skewed")
-# Untimed warm-up calls, at least, before each of the extra workloads of the
-# default line (the headline step takes exactly --warmup): after only 5, the
-# prefill workload measured about 10% slower than after 20 on the same GPU.
+# Before each extra workload of the default line (the headline step takes
+# exactly --warmup): at least this many untimed calls, and untimed calls until
+# this much wall time has passed. The GPU's clock ramps over the first ~40 ms
+# of sustained work: prefill calls took 0.73, 0.61, 0.59 and then a steady
+# 0.575 ms over the first 20-call groups of one run.
 EXTRA_WARMUP = 10
+EXTRA_WARMUP_S = 0.06
+
+
+def warm(torch, dev, fn, calls: int, seconds: float = 0.0) -> None:
+    """`calls` untimed calls of fn, then more in groups of 10 until `seconds`
+    of wall time have passed since the first."""
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        fn()
+    torch.cuda.synchronize(dev)
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize(dev)
 
 
 def main() -> int:
@@ -676,11 +691,13 @@ def main() -> int:
                 continue
             progress("%s decode" % config)
             extra[config] = run_decode(args, torch, B, W, dev, config,
-                                       warmup=max(args.warmup, EXTRA_WARMUP))
+                                       warmup=max(args.warmup, EXTRA_WARMUP),
+                                       warm_s=EXTRA_WARMUP_S)
             torch.cuda.empty_cache()
         progress("prefill")
         extra["prefill"] = run_prefill(args, torch, B, W, dev,
-                                       warmup=max(args.warmup, EXTRA_WARMUP))
+                                       warmup=max(args.warmup, EXTRA_WARMUP),
+                                       warm_s=EXTRA_WARMUP_S)
         torch.cuda.empty_cache()
         progress("36-layer step")
         rec["model_36_layers"] = run_model(args, torch, B, W, dev)

@@ -154,21 +154,19 @@ __device__ __forceinline__ int64_t block_of(const PrefillArgs& a, const int32_t*
   return (raw >= 0 && raw < a.num_blocks) ? raw : 0;
 }
 
-// Cache row of key position p: SMALL looks up p's own block, otherwise the
-// whole stage lies in the block `blk` (blocks hold at least a stage).
-template <bool SMALL>
-__device__ __forceinline__ int64_t cache_row(const PrefillArgs& a, const int32_t* bt, int64_t blk,
-                                             int p) {
-  if constexpr (SMALL) blk = block_of(a, bt, p);
-  return (blk << a.block_shift) + (p & (a.block_size - 1));
+// Cache row of key position p when blocks hold fewer keys than a stage: each
+// key looks its block up on its own.
+__device__ __forceinline__ int64_t small_block_row(const PrefillArgs& a, const int32_t* bt, int p) {
+  return (block_of(a, bt, p) << a.block_shift) + (p & (a.block_size - 1));
 }
 
-// Register loads of K (resp. V) of stage `stage`; keys at or past kmax are
-// never visible and re-read the last needed one.
-template <int D, bool SMALL>
-__device__ __forceinline__ void load_k32(const PrefillArgs& a, const int32_t* bt, int64_t blk,
-                                         int g, int kmax, int stage,
-                                         u32x4 (&kreg)[Geo<D>::KCHUNKS]) {
+// Register loads of K (resp. V) of stage `stage` for blocks smaller than a
+// stage; keys at or past kmax are never visible and re-read the last needed
+// one. (Larger blocks use scalar stage bases, in the kernel.)
+template <int D>
+__device__ __forceinline__ void load_k_small(const PrefillArgs& a, const int32_t* bt, int g,
+                                             int kmax, int stage,
+                                             u32x4 (&kreg)[Geo<D>::KCHUNKS]) {
   const int t = threadIdx.x;
   const int64_t row_elems = (int64_t)a.num_kv_heads * D;
   const uint16_t* kc = a.k_cache + (int64_t)g * D;
@@ -176,15 +174,15 @@ __device__ __forceinline__ void load_k32(const PrefillArgs& a, const int32_t* bt
   for (int i = 0; i < Geo<D>::KCHUNKS; ++i) {
     const int c = t + i * kThreads;
     const int kp = min(stage * kKT + c / (D / 8), kmax - 1);
-    kreg[i] = *reinterpret_cast<const u32x4*>(kc + cache_row<SMALL>(a, bt, blk, kp) * row_elems +
+    kreg[i] = *reinterpret_cast<const u32x4*>(kc + small_block_row(a, bt, kp) * row_elems +
                                               (c % (D / 8)) * 8);
   }
 }
 
-template <int D, bool SMALL>
-__device__ __forceinline__ void load_v32(const PrefillArgs& a, const int32_t* bt, int64_t blk,
-                                         int g, int kmax, int stage,
-                                         typename VVec<Geo<D>::VW>::T (&vreg)[2]) {
+template <int D>
+__device__ __forceinline__ void load_v_small(const PrefillArgs& a, const int32_t* bt, int g,
+                                             int kmax, int stage,
+                                             typename VVec<Geo<D>::VW>::T (&vreg)[2]) {
   typedef typename VVec<Geo<D>::VW>::T VT;
   const int t = threadIdx.x;
   const int64_t row_elems = (int64_t)a.num_kv_heads * D;
@@ -194,7 +192,7 @@ __device__ __forceinline__ void load_v32(const PrefillArgs& a, const int32_t* bt
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int kp = min(stage * kKT + 2 * pair + s, kmax - 1);
-    vreg[s] = *reinterpret_cast<const VT*>(vc + cache_row<SMALL>(a, bt, blk, kp) * row_elems +
+    vreg[s] = *reinterpret_cast<const VT*>(vc + small_block_row(a, bt, kp) * row_elems +
                                            dg * Geo<D>::VW);
   }
 }
@@ -334,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void prefill32_kernel(PrefillArgs a) {
   // rows past kmax are read as they are (same block, and the mask removes
   // their scores); V rows past kmax re-read row kmax - 1, since a zero
   // weight times a non-finite stale value would not vanish. Smaller blocks
-  // look every key up on its own (load_k32 / load_v32).
+  // look every key up on its own (load_k_small / load_v_small).
   typedef typename VVec<GG::VW>::T VT;
   const int row_e = H_kv * D;           // elements per cache row
   const int pair = threadIdx.x % 32;    // V: keys 2 pair, 2 pair + 1 of a stage
@@ -352,8 +350,8 @@ __global__ __launch_bounds__(kThreads) void prefill32_kernel(PrefillArgs a) {
   // K of stage sk (in block bk) and V of stage sv (in block bv)
   auto load_kv = [&](int sk, int64_t bk, int sv, int64_t bv) {
     if constexpr (SMALL) {
-      load_k32<D, true>(a, bt, 0, g, kmax, sk, kr);
-      load_v32<D, true>(a, bt, 0, g, kmax, sv, vr);
+      load_k_small<D>(a, bt, g, kmax, sk, kr);
+      load_v_small<D>(a, bt, g, kmax, sv, vr);
     } else {
       const int kb = sk * kKT, vb = sv * kKT;
       const uint16_t* kp =
