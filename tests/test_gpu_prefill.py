@@ -54,12 +54,12 @@ def test_prefix_cached_workload():
     check_whole_output("prefill", "prefill", out)
 
 
-def ragged_case(h_q, h_kv, d, prefix, suffix, seed):
+def ragged_case(h_q, h_kv, d, prefix, suffix, seed, bs=256):
     """Own (unshared) blocks per sequence; cached prefixes of any length."""
     rng = np.random.default_rng(seed)
     starts = np.array(prefix, dtype=np.int32)
     ends = starts + np.array(suffix, dtype=np.int32)
-    need = [-(-int(e) // 256) for e in ends]
+    need = [-(-int(e) // bs) for e in ends]
     nb = int(np.ceil(1.1 * sum(need)))
     perm = rng.permutation(nb)
     tables, pos = [], 0
@@ -67,12 +67,12 @@ def ragged_case(h_q, h_kv, d, prefix, suffix, seed):
         tables.append(perm[pos:pos + n].tolist())
         pos += n
     total = int(sum(suffix))
-    return W.PrefillCase("ragged", h_q, h_kv, d, 256, nb,
+    return W.PrefillCase("ragged", h_q, h_kv, d, bs, nb,
                          W.normal_bf16(rng, (total, h_q, d)),
                          W.normal_bf16(rng, (total, h_kv, d)),
                          W.normal_bf16(rng, (total, h_kv, d)),
-                         W.normal_bf16(rng, (nb, 256, h_kv, d)),
-                         W.normal_bf16(rng, (nb, 256, h_kv, d)),
+                         W.normal_bf16(rng, (nb, bs, h_kv, d)),
+                         W.normal_bf16(rng, (nb, bs, h_kv, d)),
                          W.pad_tables(tables), starts, ends, 1.0 / np.sqrt(d), seed)
 
 
@@ -198,3 +198,24 @@ def test_scores_far_above_the_first_keys(h_q, h_kv, d):
     ref = oracle.prefill_varlen(case.q, kref, vref, cu_q, cu_k, case.block_tables, case.scale)
     mx, mean = assert_close(out, ref, "growing keys %d/%d/%d" % (h_q, h_kv, d))
     print("  parity: max abs %.3g mean abs %.3g" % (mx, mean))
+
+
+@pytest.mark.parametrize("bs", [16, 256])
+def test_long_cached_context(bs):
+    """Chunked prefill at the end of long cached contexts (100,000 and 70,001
+    tokens, the second ending mid-block): over a thousand 64-key stages per
+    workgroup, hundreds to thousands of table entries per sequence, per-key
+    lookups (blocks of 16) and one scalar base per stage (blocks of 256).
+    q is scaled by 8 (exact in bf16) so that each row's weight sits on a few
+    of its keys and the output depends on finding them (with unscaled random
+    data a long context averages to near zero); V by 1/4 (exact) so that the
+    bf16 rounding of an output near one V row stays inside the bound.
+    Every row vs the oracle."""
+    case = ragged_case(8, 2, 128, [100000, 70001], [8, 3], seed=97 + bs, bs=bs)
+    case.q = W.round_to_bf16_bits(oracle.bf16_bits_to_f64(case.q) * 8.0)
+    case.v_cache = W.round_to_bf16_bits(oracle.bf16_bits_to_f64(case.v_cache) * 0.25)
+    case.v_new = W.round_to_bf16_bits(oracle.bf16_bits_to_f64(case.v_new) * 0.25)
+    out, kref, vref, cu_q, cu_k = run_prefill_step(case)
+    ref = oracle.prefill_varlen(case.q, kref, vref, cu_q, cu_k, case.block_tables, case.scale)
+    mx, mean = assert_close(out, ref, "long cached context, block %d" % bs)
+    print("  parity: max abs %.3g mean abs %.3g (max |ref| %.3g)" % (mx, mean, np.abs(ref).max()))
