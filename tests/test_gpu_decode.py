@@ -250,3 +250,23 @@ def test_explicit_long_partitions_on_the_ordered_grid(partition_blocks):
     out, caches, slots, before = run_decode_step(case, partition_blocks=partition_blocks)
     kc_ref, vc_ref = check_store(case, caches, slots, before)
     check_decode(case, out, kc_ref, vc_ref)
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(8, 2), (16, 1)])
+def test_one_sequence_spans_every_grab(h_q, h_kv):
+    """One 200,000-token sequence beside two short ones: the long one covers
+    nearly every grab of the launch, so its pieces (about 256 per kv-head
+    group) are merged by one wave at the end; vector path (G = 4) and
+    matrix-core path (G = 16). q is scaled by 8 so that each row's weight
+    sits on a few keys somewhere in the 200,000 (random data would average
+    to near zero), V by 1/4 so that bf16 rounding of an output near one V row
+    stays inside the bound; both exact in bf16. Every row vs the oracle."""
+    lens = [200000, 3, 700]
+    case = W.decode_case(h_q, h_kv, 128, lens, seed=85 + h_q)
+    case.q = W.round_to_bf16_bits(oracle.bf16_bits_to_f64(case.q) * 8.0)
+    case.v_cache = W.round_to_bf16_bits(oracle.bf16_bits_to_f64(case.v_cache) * 0.25)
+    case.v_new = W.round_to_bf16_bits(oracle.bf16_bits_to_f64(case.v_new) * 0.25)
+    out, caches, slots, before = run_decode_step(case)
+    kc_ref, vc_ref = check_store(case, caches, slots, before)
+    ref = check_decode(case, out, kc_ref, vc_ref)
+    _log("  max |ref| %.3g" % np.abs(ref).max())
