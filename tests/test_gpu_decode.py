@@ -270,3 +270,20 @@ def test_one_sequence_spans_every_grab(h_q, h_kv):
     kc_ref, vc_ref = check_store(case, caches, slots, before)
     ref = check_decode(case, out, kc_ref, vc_ref)
     _log("  max |ref| %.3g" % np.abs(ref).max())
+
+
+@pytest.mark.parametrize("bs", [16, 256])
+def test_more_pairs_than_arrival_counters(bs):
+    """8,200 sequences x 8 kv-heads = 65,600 (sequence, kv-head) pairs, more
+    than the 65,536 arrival counters of the workspace header: the call takes
+    the partitioned grid on its own. Lengths 1..64 with padding rows, block
+    sizes 16 and 256; every row vs the oracle."""
+    rng = np.random.default_rng(86)
+    lens = rng.integers(1, 64 + 1, size=8200)
+    pad = [5, 4000, 8199]
+    lens[pad] = 0
+    case = W.decode_case(8, 8, 64, lens, seed=87, block_size=bs)
+    out, caches, slots, before = run_decode_step(case)
+    kc_ref, vc_ref = check_store(case, caches, slots, before)
+    check_decode(case, out, kc_ref, vc_ref)
+    assert np.all(out[pad] == 0)
